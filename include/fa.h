@@ -1,0 +1,97 @@
+/*
+ * fa.h - C ABI of the exact-attention forward library (libfa.so), gfx950.
+ *
+ * The operation is exact softmax attention computed tile by tile with the
+ * online-softmax recurrence, so the N x N score matrix is never written to
+ * memory:
+ *
+ *   S = scale * Q K^T            (per batch b and head h)
+ *   S_ij = -inf where causal and j > i (lower-triangular mask)
+ *   O = softmax_rows(S) V,  LSE_i = ln sum_j exp(S_ij)
+ *
+ * Sources: the standard three-step form and its [batch, heads, seq, head_dim]
+ * layout and -inf mask are section 1.1 of "2.3 FlashAttention and IO-aware
+ * attention" (aiknowledge.cn); the blockwise recurrence (running max m,
+ * running sum l, rescale of the output accumulator, final O / l) is
+ * ``flash_attention_forward`` on the flash_attention.py teaching page
+ * (forceinjection.github.io); the scale and causal arguments mirror
+ * ``softmax_scale`` / ``causal`` of the packed call in section 5.2 of the
+ * flash-attn 2.8.3 build guide (intelliparadigm.com). LSE is the row
+ * statistic m + ln l that the recurrence carries; it is written so that a
+ * backward pass or a merge of partial results can use it.
+ */
+#ifndef FA_H
+#define FA_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element type of q, k, v and o. lse is always float32. */
+typedef enum {
+    FA_F16 = 0,  /* IEEE binary16 */
+    FA_BF16 = 1, /* bfloat16 */
+    FA_F32 = 2   /* IEEE binary32; computed in fp32 end to end */
+} fa_dtype;
+
+typedef enum {
+    FA_OK = 0,
+    FA_ERR_NULL = -1,    /* a required pointer is NULL */
+    FA_ERR_SHAPE = -2,   /* a size is negative or too large */
+    FA_ERR_HEADDIM = -3, /* d is not 64, 128 or 256 */
+    FA_ERR_DTYPE = -4,   /* dtype is not an fa_dtype */
+    FA_ERR_ALIGN = -5,   /* q, k, v, o not 16-byte aligned, or lse not 4-byte aligned */
+    FA_ERR_ARG = -6,     /* causal not 0/1, scale not finite, or outputs overlap inputs */
+    FA_ERR_LAUNCH = -7   /* the HIP runtime rejected the kernel launch */
+} fa_status;
+
+/*
+ * fa_fwd - enqueue one attention forward pass on `stream`.
+ *
+ * q, k, v  device pointers, [B, H, N, d] contiguous (d fastest), element type
+ *          `dtype`. Read only; they may alias one another.
+ * o        device pointer, [B, H, N, d] contiguous, element type `dtype`;
+ *          written with O rounded to nearest even.
+ * lse      device pointer, [B, H, N] contiguous float32; written with the
+ *          natural-log LSE of each query row.
+ * B, H, N  batch, heads, sequence length (queries and keys have the same N).
+ * d        head dimension: 64, 128 or 256.
+ * scale    multiplies Q K^T before the softmax; finite (0 gives uniform
+ *          weights). Callers wanting the usual default pass 1/sqrt(d).
+ * causal   0: every key is visible; 1: query i sees keys j <= i.
+ * stream   a hipStream_t, or NULL for the default stream.
+ *
+ * Ownership: the caller allocates and owns every buffer. The library
+ * allocates nothing, keeps no state between calls and is reentrant.
+ * o and lse must not overlap q, k or v.
+ *
+ * Synchronisation: asynchronous. The kernel is enqueued and the call returns;
+ * a fault inside it surfaces at the caller's next synchronisation.
+ *
+ * Errors: all argument checks run on the host before any HIP call, and a
+ * failed check returns its negative fa_status without touching the GPU. If
+ * B*H*N == 0 the call returns FA_OK without launching (pointers are then not
+ * checked). FA_ERR_LAUNCH is returned if the runtime reports an error right
+ * after the launch.
+ */
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+           int B, int H, int N, int d, float scale, int causal, int dtype,
+           void* stream);
+
+/* Static text for a status code (never NULL). */
+const char* fa_strerror(int status);
+
+/*
+ * fa_fwd_grid - host-only query of the launch shape fa_fwd would use:
+ * writes the number of workgroups and the query rows per workgroup. Returns
+ * the same status fa_fwd's argument checks would (pointers excepted). Used
+ * to relate kernel timings to work units; makes no HIP call.
+ */
+int fa_fwd_grid(int B, int H, int N, int d, int causal, int dtype,
+                long long* workgroups, int* rows_per_workgroup);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H */

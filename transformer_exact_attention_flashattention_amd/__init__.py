@@ -1,0 +1,171 @@
+"""Exact-attention forward pass on MI355X (gfx950): thin Python binding.
+
+Every step of the computation runs in the HIP kernels of ``libfa.so``; this
+module only marshals arguments (device pointers, sizes, the current stream)
+into the C ABI declared in ``include/fa.h``. There is no CPU fallback: if the
+library is missing or the tensors are not on a GPU, the calls raise.
+
+API (names follow the flash-attn interface that section 5.2 / 10.1 of the
+flash-attn 2.8.3 build guide, intelliparadigm.com, calls):
+
+* ``fwd(q, k, v, softmax_scale=None, causal=False) -> (o, lse)`` with
+  q, k, v of shape [B, H, N, d] (the layout of section 1.1 of "2.3
+  FlashAttention and IO-aware attention"), contiguous, on one GPU, all of
+  dtype float16, bfloat16 or float32; ``softmax_scale=None`` means 1/sqrt(d).
+* ``flash_attn_qkvpacked_func(qkv, dropout_p=0.0, softmax_scale=None,
+  causal=False) -> (o, lse)`` for a packed tensor [B, N, 3, H, d]; it splits
+  and transposes the packed tensor into three [B, H, N, d] tensors (a copy)
+  and calls ``fwd``; o and lse come back as [B, H, N, d] and [B, H, N].
+* ``fa_fwd(...)``: the raw C entry point with the same arguments as the C
+  function, for callers that manage their own pointers and streams.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+from .build import LIB_PATH
+
+FA_F16, FA_BF16, FA_F32 = 0, 1, 2
+STATUS = {
+    0: "FA_OK",
+    -1: "FA_ERR_NULL",
+    -2: "FA_ERR_SHAPE",
+    -3: "FA_ERR_HEADDIM",
+    -4: "FA_ERR_DTYPE",
+    -5: "FA_ERR_ALIGN",
+    -6: "FA_ERR_ARG",
+    -7: "FA_ERR_LAUNCH",
+}
+# Every symbol include/fa.h declares.
+EXPORTS = ("fa_fwd", "fa_strerror", "fa_fwd_grid")
+
+_lib = None
+
+
+class FaError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS.get(status, status)}: {message}")
+        self.status = status
+
+
+def lib() -> ctypes.CDLL:
+    """Load libfa.so (once). Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"HIP library {LIB_PATH} is not built; run "
+                "`python -c 'import __graft_entry__ as g; g.build()'` first"
+            )
+        h = ctypes.CDLL(LIB_PATH)
+        h.fa_fwd.restype = ctypes.c_int
+        h.fa_fwd.argtypes = [
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+            ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_float,
+            ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+        ]
+        h.fa_strerror.restype = ctypes.c_char_p
+        h.fa_strerror.argtypes = [ctypes.c_int]
+        h.fa_fwd_grid.restype = ctypes.c_int
+        h.fa_fwd_grid.argtypes = [
+            ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+            ctypes.POINTER(ctypes.c_longlong), ctypes.POINTER(ctypes.c_int),
+        ]
+        _lib = h
+    return _lib
+
+
+def strerror(status: int) -> str:
+    return lib().fa_strerror(int(status)).decode()
+
+
+def fa_fwd(q, k, v, o, lse, B, H, N, d, scale, causal, dtype, stream=None) -> int:
+    """Raw call of the C entry point; pointers are ints (device addresses)."""
+    return lib().fa_fwd(q, k, v, o, lse, B, H, N, d, scale, causal, dtype, stream)
+
+
+def grid(B, H, N, d, causal, dtype):
+    """(workgroups, query rows per workgroup) of the launch fa_fwd would make."""
+    wg = ctypes.c_longlong(0)
+    rows = ctypes.c_int(0)
+    st = lib().fa_fwd_grid(B, H, N, d, int(causal), dtype, ctypes.byref(wg), ctypes.byref(rows))
+    if st != 0:
+        raise FaError(st, strerror(st))
+    return wg.value, rows.value
+
+
+def _dtype_code(t):
+    import torch
+
+    codes = {torch.float16: FA_F16, torch.bfloat16: FA_BF16, torch.float32: FA_F32}
+    if t.dtype not in codes:
+        raise NotImplementedError(f"dtype {t.dtype} is not supported (float16, bfloat16, float32)")
+    return codes[t.dtype]
+
+
+def fwd(q, k, v, softmax_scale=None, causal=False, out=None, lse=None):
+    """Attention forward on the GPU: returns (o [B,H,N,d], lse [B,H,N] fp32)."""
+    import torch
+
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{name} must be a torch.Tensor")
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be on a GPU (no CPU path exists)")
+        if t.dim() != 4:
+            raise ValueError(f"{name} must be [B, H, N, d], got shape {tuple(t.shape)}")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if not (q.shape == k.shape == v.shape):
+        raise ValueError(f"q, k, v shapes differ: {tuple(q.shape)} {tuple(k.shape)} {tuple(v.shape)}")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q, k, v must share one dtype")
+    if not (q.device == k.device == v.device):
+        raise ValueError("q, k, v must be on one device")
+    code = _dtype_code(q)
+    B, H, N, d = q.shape
+    if d not in (64, 128, 256):
+        raise NotImplementedError(f"head dimension {d} is not supported (64, 128, 256)")
+    scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    if out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous() or out.device != q.device:
+        raise ValueError("out must be a contiguous tensor like q")
+    if lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous() or lse.device != q.device:
+        raise ValueError("lse must be a contiguous float32 tensor [B, H, N] on q's device")
+    with torch.cuda.device(q.device):
+        stream = torch.cuda.current_stream().cuda_stream
+        st = lib().fa_fwd(
+            q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+            B, H, N, d, scale, int(bool(causal)), code, stream,
+        )
+    if st != 0:
+        raise FaError(st, strerror(st))
+    return out, lse
+
+
+def flash_attn_qkvpacked_func(qkv, dropout_p=0.0, softmax_scale=None, causal=False,
+                              window_size=(-1, -1), alibi_slopes=None, deterministic=False):
+    """Packed-QKV entry: qkv [B, N, 3, H, d] -> (o [B,H,N,d], lse [B,H,N])."""
+    if dropout_p != 0.0:
+        raise NotImplementedError("dropout is not supported")
+    if tuple(window_size) != (-1, -1):
+        raise NotImplementedError("local (windowed) attention is not supported")
+    if alibi_slopes is not None:
+        raise NotImplementedError("ALiBi is not supported")
+    if qkv.dim() != 5 or qkv.shape[2] != 3:
+        raise ValueError(f"qkv must be [B, N, 3, H, d], got {tuple(qkv.shape)}")
+    q, k, v = (qkv[:, :, i].permute(0, 2, 1, 3).contiguous() for i in range(3))
+    return fwd(q, k, v, softmax_scale=softmax_scale, causal=causal)
+
+
+def flash_attn_func(q, k, v, dropout_p=0.0, softmax_scale=None, causal=False):
+    """Same as ``fwd`` (q, k, v in [B, H, N, d]); dropout must be 0."""
+    if dropout_p != 0.0:
+        raise NotImplementedError("dropout is not supported")
+    return fwd(q, k, v, softmax_scale=softmax_scale, causal=causal)

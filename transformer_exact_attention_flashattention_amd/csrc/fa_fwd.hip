@@ -1,0 +1,129 @@
+// fa_fwd.hip - C ABI of the attention forward library: argument checks,
+// kernel selection and launch. Declarations and the contract are in
+// include/fa.h; the kernels are in fa_kernels.h.
+#include <hip/hip_runtime.h>
+
+#include <climits>
+#include <cmath>
+#include <cstdint>
+
+#include "fa.h"
+#include "fa_kernels.h"
+
+namespace {
+
+typedef void (*fwd16_fn)(const uint16_t*, const uint16_t*, const uint16_t*, uint16_t*, float*, int, int,
+                         int, float);
+typedef void (*fwd32_fn)(const float*, const float*, const float*, float*, float*, int, int, int,
+                         float);
+
+template <class T>
+fwd16_fn pick16(int d, bool causal) {
+  switch (d) {
+    case 64: return causal ? fa::fwd16_kernel<T, 64, true> : fa::fwd16_kernel<T, 64, false>;
+    case 128: return causal ? fa::fwd16_kernel<T, 128, true> : fa::fwd16_kernel<T, 128, false>;
+    case 256: return causal ? fa::fwd16_kernel<T, 256, true> : fa::fwd16_kernel<T, 256, false>;
+  }
+  return nullptr;
+}
+
+fwd32_fn pick32(int d, bool causal) {
+  switch (d) {
+    case 64: return causal ? fa::fwd32_kernel<64, true> : fa::fwd32_kernel<64, false>;
+    case 128: return causal ? fa::fwd32_kernel<128, true> : fa::fwd32_kernel<128, false>;
+    case 256: return causal ? fa::fwd32_kernel<256, true> : fa::fwd32_kernel<256, false>;
+  }
+  return nullptr;
+}
+
+// Checks that do not involve pointers. Fills the launch shape on success.
+int check_shape(int B, int H, int N, int d, int causal, int dtype, long long* nblocks, int* nqt) {
+  if (B < 0 || H < 0 || N < 0 || d < 0) return FA_ERR_SHAPE;
+  if (dtype != FA_F16 && dtype != FA_BF16 && dtype != FA_F32) return FA_ERR_DTYPE;
+  if (d != 64 && d != 128 && d != 256) return FA_ERR_HEADDIM;
+  if (causal != 0 && causal != 1) return FA_ERR_ARG;
+  // Row offsets inside one head are computed in 32-bit arithmetic before
+  // widening, so keep N comfortably below 2^30.
+  if (N > (1 << 30) - fa::kBr) return FA_ERR_SHAPE;
+  const long long q_tiles = (N + fa::kBr - 1) / fa::kBr;
+  const long long blocks = (long long)B * (long long)H * q_tiles;
+  if (blocks > INT_MAX) return FA_ERR_SHAPE;
+  *nblocks = blocks;
+  *nqt = (int)q_tiles;
+  return FA_OK;
+}
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+  return x < y + nb && y < x + na;
+}
+
+}  // namespace
+
+extern "C" const char* fa_strerror(int status) {
+  switch (status) {
+    case FA_OK: return "success";
+    case FA_ERR_NULL: return "a required pointer is NULL";
+    case FA_ERR_SHAPE: return "a size is negative or too large";
+    case FA_ERR_HEADDIM: return "head dimension must be 64, 128 or 256";
+    case FA_ERR_DTYPE: return "dtype must be FA_F16, FA_BF16 or FA_F32";
+    case FA_ERR_ALIGN: return "q, k, v, o must be 16-byte aligned and lse 4-byte aligned";
+    case FA_ERR_ARG: return "causal must be 0 or 1, scale finite, and o/lse must not overlap q/k/v";
+    case FA_ERR_LAUNCH: return "the HIP runtime rejected the kernel launch";
+  }
+  return "unknown fa_status";
+}
+
+extern "C" int fa_fwd_grid(int B, int H, int N, int d, int causal, int dtype, long long* workgroups,
+                           int* rows_per_workgroup) {
+  long long nblocks = 0;
+  int nqt = 0;
+  const int st = check_shape(B, H, N, d, causal, dtype, &nblocks, &nqt);
+  if (st != FA_OK) return st;
+  if (workgroups) *workgroups = nblocks;
+  if (rows_per_workgroup) *rows_per_workgroup = fa::kBr;
+  return FA_OK;
+}
+
+extern "C" int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                      int N, int d, float scale, int causal, int dtype, void* stream) {
+  long long nblocks = 0;
+  int nqt = 0;
+  int st = check_shape(B, H, N, d, causal, dtype, &nblocks, &nqt);
+  if (st != FA_OK) return st;
+  if (!std::isfinite(scale)) return FA_ERR_ARG;
+  if (nblocks == 0) return FA_OK;  // B*H*N == 0: nothing to do
+  if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
+  if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o) & 15) return FA_ERR_ALIGN;
+  if ((uintptr_t)lse & 3) return FA_ERR_ALIGN;
+
+  const size_t esz = dtype == FA_F32 ? 4 : 2;
+  const size_t elems = (size_t)B * H * N * d;
+  const size_t tbytes = elems * esz;
+  const size_t lbytes = (size_t)B * H * N * sizeof(float);
+  const void* ins[3] = {q, k, v};
+  for (const void* in : ins) {
+    if (overlaps(o, tbytes, in, tbytes) || overlaps(lse, lbytes, in, tbytes)) return FA_ERR_ARG;
+  }
+  if (overlaps(o, tbytes, lse, lbytes)) return FA_ERR_ARG;
+
+  // log2(e) is folded into the scale: exp(x * scale) == exp2(x * c).
+  const float c = (float)((double)scale * 1.4426950408889634074);
+  int n_arg = N, nqt_arg = nqt, nb_arg = (int)nblocks;
+  float c_arg = c;
+  void* args[] = {(void*)&q, (void*)&k, (void*)&v, (void*)&o, (void*)&lse,
+                  (void*)&n_arg, (void*)&nqt_arg, (void*)&nb_arg, (void*)&c_arg};
+
+  const void* fn = nullptr;
+  if (dtype == FA_F32) {
+    fn = (const void*)pick32(d, causal != 0);
+  } else if (dtype == FA_BF16) {
+    fn = (const void*)pick16<fa::Bf16>(d, causal != 0);
+  } else {
+    fn = (const void*)pick16<fa::F16>(d, causal != 0);
+  }
+  if (!fn) return FA_ERR_HEADDIM;
+  const hipError_t e = hipLaunchKernel(fn, dim3((unsigned)nblocks), dim3(fa::kThreads), args, 0,
+                                       (hipStream_t)stream);
+  return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
