@@ -126,7 +126,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-heads", type=int, default=2)
+    ap.add_argument("--cpu-heads", type=int, default=10)
     ap.add_argument("--no-secondary", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
