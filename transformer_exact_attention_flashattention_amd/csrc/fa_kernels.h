@@ -39,6 +39,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace fa {
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
@@ -169,152 +171,362 @@ __device__ __forceinline__ float online_softmax(f32x16& s0, f32x16& s1, float c,
 
 // ---------------------------------------------------------------------------
 // fp16 / bf16 kernel.
-// LDS: ks = K tile [64 rows][D], row m holds key sigma(m), 16-byte chunk ch of
-// a row stored at chunk position ch ^ (m & 7); vt = V^T tile [D rows][64 keys]
-// (128 bytes per row), chunk ch (keys 8ch..8ch+7) at position ch ^ (d & 7).
+//
+// LDS holds two stages of K and two of V (separate arrays, so the compiler
+// can tell a copy into one stage from reads of the other). Tile rows are keys
+// in order; K rows are 2D + 16 bytes apart, V rows 2D + 64 bytes apart. The
+// padding puts the 16 rows read by one 16-lane ds_read_b128 phase (K) and
+// the 4 rows x 64 bytes read by one 32-lane ds_read_b64_tr_b16 phase (V) on
+// distinct banks, and lets every LDS read use one base register plus
+// immediate offsets. Tiles are copied by buffer_load_dwordx4 ... lds: each
+// wave instruction fills 1 KiB of LDS, 16 bytes per lane in lane order, and
+// each lane fetches the global chunk that belongs at its slot (pad slots
+// fetch a duplicate of a real chunk). Rows past the end of the sequence
+// fetch the last real row instead (their scores are masked, and the
+// duplicate keeps V finite).
+
+template <int D>
+struct Geo16 {
+  static constexpr int kRowB = 2 * D;         // bytes of one K/V row in memory
+  static constexpr int kSK = kRowB + 16;      // LDS K row stride
+  static constexpr int kSV = kRowB + 64;      // LDS V row stride
+  static constexpr int kKT = kBc * kSK;       // LDS bytes of a K tile
+  static constexpr int kVT = kBc * kSV;       // LDS bytes of a V tile
+  static constexpr int kKI = kKT / 1024;      // 1 KiB copy instructions per K tile
+  static constexpr int kVI = kVT / 1024;
+  static constexpr int kKPW = (kKI + 3) / 4;  // per wave (upper bound)
+  static constexpr int kVPW = (kVI + 3) / 4;
+  static_assert(kKT % 1024 == 0 && kVT % 1024 == 0, "tiles are whole copy blocks");
+};
+
+// Source byte offset (relative to the tile's first row) of LDS slot t of a
+// tile whose rows are `stride` bytes apart.
+template <int D, int STRIDE>
+__device__ __forceinline__ uint32_t tile_src(int t) {
+  constexpr int R = STRIDE / 16;  // 16-byte slots per LDS row
+  const int m = t / R;
+  int q = t - m * R;
+  if (q >= D / 8) q = 0;  // pad slot
+  return (uint32_t)(m * 2 * D + 16 * q);
+}
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// Marks a value as used here (emits no instruction). Keeps the compiler from
+// sinking the code that produces it past this point, e.g. into the next loop
+// iteration, which would undo the interleaving of the matrix-core and vector
+// work.
+// (The host pass of hipcc parses device code too; it has no "v" registers.)
+#if defined(__HIP_DEVICE_COMPILE__)
+__device__ __forceinline__ void pin(u32x4& x) { asm volatile("" : "+v"(x)); }
+__device__ __forceinline__ void pin(float& x) { asm volatile("" : "+v"(x)); }
+#else
+__device__ __forceinline__ void pin(u32x4&) {}
+__device__ __forceinline__ void pin(float&) {}
+#endif
+
+__device__ __forceinline__ lds_ptr_t as_lds(const void* p) { return (lds_ptr_t)p; }
+
+// max / sum over the lane pair (l, l ^ 32): v_permlane32_swap exchanges the
+// upper half of its first operand with the lower half of its second.
+__device__ __forceinline__ float pair_max(float x) {
+  const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+
+__device__ __forceinline__ float pair_sum(float x) {
+  const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+
+// The running max used as the exponent reference only moves when a tile's
+// max exceeds it by more than kTau (log2 units). The result is the same in
+// exact arithmetic for any reference (the final division by the running sum
+// cancels it); skipping small moves spares the rescale of the output
+// accumulator on most tiles, at the price of P values up to 2^kTau.
+constexpr float kTau = 8.0f;
+
+constexpr uint32_t kBufWord3 = 0x00020000u;  // raw buffer, 32-bit data format
+
+// Copies one tile (its first row at `src`, `nvalid` rows of the sequence
+// left from there) into LDS at `dst`: wave w issues copy blocks w, w + 4, ...
+// of the NBLK 1 KiB blocks; off[i] is the lane's source offset for its i-th
+// block. In a ragged tile, rows past the end re-fetch the last real row.
+template <int D, int NBLK>
+__device__ __forceinline__ void copy_tile(const unsigned char* src, int nvalid, unsigned char* dst,
+                                          const uint32_t (&off)[(NBLK + 3) / 4], int wave) {
+#if defined(__HIP_DEVICE_COMPILE__)  // buffer resources exist only on the device side
+  constexpr int kRowB = 2 * D;
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)src, (short)0, kBc * kRowB, kBufWord3);
+  if (nvalid >= kBc) {
+#pragma unroll
+    for (int i = 0; i < (NBLK + 3) / 4; ++i)
+      if (wave + 4 * i < NBLK)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, as_lds(dst + 1024 * (wave + 4 * i)), 16, off[i], 0, 0, 0);
+  } else {
+    const uint32_t row_end = (uint32_t)nvalid * kRowB;
+    const uint32_t last_row = row_end - kRowB;
+#pragma unroll
+    for (int i = 0; i < (NBLK + 3) / 4; ++i)
+      if (wave + 4 * i < NBLK) {
+        const uint32_t o = off[i] >= row_end ? last_row + (off[i] & (kRowB - 1)) : off[i];
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, as_lds(dst + 1024 * (wave + 4 * i)), 16, o, 0, 0, 0);
+      }
+  }
+#endif
+}
+
+// Scheduling masks of __builtin_amdgcn_sched_group_barrier.
+constexpr int kSchedValu = 0x0002 | 0x0400;  // VALU and transcendental
+constexpr int kSchedMfma = 0x0008;
+constexpr int kSchedDsRead = 0x0100;
+
 template <class T, int D, bool CAUSAL>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
-                          amdgpu_waves_per_eu(1, 1)))
+                          amdgpu_waves_per_eu(D >= 256 ? 1 : 2, D >= 256 ? 1 : 2)))
 void fwd16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                   const uint16_t* __restrict__ V, uint16_t* __restrict__ O,
                   float* __restrict__ LSE, int N, int nqt, int nblocks, float c) {
-  constexpr int DCH = D / 8;                        // 16-byte chunks per K/V row
-  constexpr int KS_BYTES = kBc * D * 2;
-  constexpr int VT_BYTES = D * kBc * 2;
-  constexpr int KCH = kBc * DCH / kThreads;         // K chunks staged per thread
-  constexpr int KPU = D >= 128 ? 4 : 2;             // keys per V transpose unit
-  constexpr int VGROUPS = kBc / KPU;                // key groups per tile
-  constexpr int VUNITS = VGROUPS * DCH / kThreads;  // V units per thread
-  static_assert(KCH * kThreads == kBc * DCH, "K tile split");
-  static_assert(VUNITS * kThreads == VGROUPS * DCH, "V tile split");
-
-  __shared__ __attribute__((aligned(16))) unsigned char smem[KS_BYTES + VT_BYTES];
-  unsigned char* const ks = smem;
-  unsigned char* const vt = smem + KS_BYTES;
+  using G = Geo16<D>;
+  typedef short s16x4 __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) s16x4* lds_s16x4_t;
+  __shared__ __attribute__((aligned(1024))) unsigned char k0s[G::kKT];
+  __shared__ __attribute__((aligned(1024))) unsigned char k1s[G::kKT];
+  __shared__ __attribute__((aligned(1024))) unsigned char v0s[G::kVT];
+  __shared__ __attribute__((aligned(1024))) unsigned char v1s[G::kVT];
 
   int bh, qt;
   decode_block(nblocks, nqt, CAUSAL, bh, qt);
   const size_t base = (size_t)bh * (size_t)N * D;
   Q += base;
-  K += base;
-  V += base;
   O += base;
   LSE += (size_t)bh * N;
+  const unsigned char* const kg = (const unsigned char*)(K + base);
+  const unsigned char* const vg = (const unsigned char*)(V + base);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 31;
   const int hh = lane >> 5;
   const int q0 = qt * kBr + wave * 32;
   const int qrow = q0 + n;
 
   // Q^T as B operands: lane (n, hh), k-step s holds Q[qrow][16s + 8hh .. +7].
+  // A negative scale is folded into Q (an exact sign flip) so that c >= 0.
+  // c == 0 becomes the smallest normal float: visible scores then still give
+  // exp2(S c - m) == exp2(-m) to within rounding for any |S| < 2^100, and a
+  // masked score (-inf) still gives 0.
+  const uint32_t qflip = c < 0.f ? 0x80008000u : 0u;
+  c = fmaxf(fabsf(c), 1.17549435e-38f);
   u32x4 qf[D / 16];
 #pragma unroll
-  for (int s = 0; s < D / 16; ++s)
+  for (int s = 0; s < D / 16; ++s) {
     qf[s] = qrow < N ? *(const u32x4*)(Q + (size_t)qrow * D + 16 * s + 8 * hh) : u32x4{0, 0, 0, 0};
+    qf[s] ^= qflip;
+  }
 
-  const int nkt_all = (N + kBc - 1) / kBc;
-  const int nkt = CAUSAL ? min(nkt_all, (qt * kBr + kBr - 1) / kBc + 1) : nkt_all;
+  const int nkt = CAUSAL ? min((N + kBc - 1) / kBc, (qt * kBr + kBr - 1) / kBc + 1) : (N + kBc - 1) / kBc;
+  const int nfull = CAUSAL ? min(2 * qt, N / kBc) : N / kBc;  // leading tiles no row of the block masks
 
-  u32x4 kreg[KCH];
-  u32x4 vreg[VUNITS][KPU];
+  // Tile-invariant source offsets of this lane's copy slots.
+  uint32_t koff[G::kKPW], voff[G::kVPW];
+#pragma unroll
+  for (int i = 0; i < G::kKPW; ++i) koff[i] = tile_src<D, G::kSK>(64 * (wave + 4 * i) + lane);
+#pragma unroll
+  for (int i = 0; i < G::kVPW; ++i) voff[i] = tile_src<D, G::kSV>(64 * (wave + 4 * i) + lane);
 
-  auto gload = [&](int kt) {
-    const int k0 = kt * kBc;
-#pragma unroll
-    for (int i = 0; i < KCH; ++i) {
-      const int g = tid + i * kThreads;
-      const int key = g / DCH, ch = g % DCH;
-      kreg[i] = (k0 + key < N) ? *(const u32x4*)(K + (size_t)(k0 + key) * D + ch * 8) : u32x4{0, 0, 0, 0};
-    }
-#pragma unroll
-    for (int u = 0; u < VUNITS; ++u) {
-      const int unit = tid + u * kThreads;
-      const int kg = unit % VGROUPS, dg = unit / VGROUPS;
-#pragma unroll
-      for (int j = 0; j < KPU; ++j) {
-        const int key = k0 + kg * KPU + j;
-        vreg[u][j] = key < N ? *(const u32x4*)(V + (size_t)key * D + dg * 8) : u32x4{0, 0, 0, 0};
-      }
-    }
+  auto issue_k = [&](int kt, unsigned char* dst) {
+    copy_tile<D, G::kKI>(kg + (size_t)kt * kBc * G::kRowB, N - kt * kBc, dst, koff, wave);
+  };
+  auto issue_v = [&](int kt, unsigned char* dst) {
+    copy_tile<D, G::kVI>(vg + (size_t)kt * kBc * G::kRowB, N - kt * kBc, dst, voff, wave);
   };
 
-  auto swrite = [&]() {
-#pragma unroll
-    for (int i = 0; i < KCH; ++i) {
-      const int g = tid + i * kThreads;
-      const int key = g / DCH, ch = g % DCH;
-      const int m = sigma(key);
-      *(u32x4*)(ks + m * (D * 2) + ((ch ^ (m & 7)) << 4)) = kreg[i];
-    }
-#pragma unroll
-    for (int u = 0; u < VUNITS; ++u) {
-      const int unit = tid + u * kThreads;
-      const int kg = unit % VGROUPS, dg = unit / VGROUPS;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int d = dg * 8 + e;
-        const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
-        const int w = e >> 1;
-        if constexpr (KPU == 4) {
-          u32x2 out;
-          out.x = __builtin_amdgcn_perm(vreg[u][1][w], vreg[u][0][w], sel);
-          out.y = __builtin_amdgcn_perm(vreg[u][3][w], vreg[u][2][w], sel);
-          *(u32x2*)(vt + d * (kBc * 2) + (((kg >> 1) ^ (d & 7)) << 4) + ((kg & 1) << 3)) = out;
-        } else {
-          const uint32_t out = __builtin_amdgcn_perm(vreg[u][1][w], vreg[u][0][w], sel);
-          *(uint32_t*)(vt + d * (kBc * 2) + (((kg >> 2) ^ (d & 7)) << 4) + ((kg & 3) << 2)) = out;
-        }
-      }
-    }
-  };
+  // Per-lane LDS read bases. K: MFMA row n holds key sigma(n) (second tile:
+  // +32), chunk hh. V (transposed read): 16-lane block b addresses keys
+  // 8*(b>>1) + (lane&15)/4 and columns 16*(b&1) + 4*(lane&3).
+  const int kofs = sigma(n) * G::kSK + 16 * hh;
+  const int vb = lane >> 4, vj = lane & 15;
+  const int vofs = (8 * (vb >> 1) + (vj >> 2)) * G::kSV + 32 * (vb & 1) + 8 * (vj & 3);
 
   float m_run = -INFINITY, l_run = 0.f;
   f32x16 acc[D / 32];
 #pragma unroll
   for (int t = 0; t < D / 32; ++t) acc[t] = f32x16{};
+  f32x16 sc0, sc1;  // raw scores of the tile being turned into P
 
-  gload(0);
-  for (int kt = 0; kt < nkt; ++kt) {
-    swrite();
-    __syncthreads();
-    if (kt + 1 < nkt) gload(kt + 1);
-    const int kbase = kt * kBc;
-    if (!CAUSAL || kbase <= q0 + 31) {
-      f32x16 s0 = {}, s1 = {};
-      const unsigned char* kr0 = ks + n * (D * 2);
-      const unsigned char* kr1 = ks + (32 + n) * (D * 2);
+  // S_t = K_t Q^T into sc0 (keys 0..31 of the tile) and sc1 (keys 32..63):
+  // 4 K reads ahead, then one MFMA and one read in turn.
+  auto s_tile = [&](const unsigned char* ks) {
+    sc0 = f32x16{};
+    sc1 = f32x16{};
+    const unsigned char* kp = ks + kofs;
 #pragma unroll
-      for (int s = 0; s < D / 16; ++s) {
-        const int off = ((2 * s + hh) ^ (n & 7)) << 4;
-        s0 = T::mfma(*(const u32x4*)(kr0 + off), qf[s], s0);
-        s1 = T::mfma(*(const u32x4*)(kr1 + off), qf[s], s1);
-      }
-      const float alpha = online_softmax<CAUSAL>(s0, s1, c, kbase, qrow, q0, N, hh, 1, m_run, l_run);
-      // P^T as B operands: chunk cc covers keys 16cc..16cc+15 of the tile.
-      u32x4 pf[4];
+    for (int s = 0; s < D / 16; ++s) {
+      sc0 = T::mfma(*(const u32x4*)(kp + 32 * s), qf[s], sc0);
+      sc1 = T::mfma(*(const u32x4*)(kp + 32 * G::kSK + 32 * s), qf[s], sc1);
+    }
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 4, 0);
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        pf[0][w] = T::pack(s0[2 * w], s0[2 * w + 1]);
-        pf[1][w] = T::pack(s0[8 + 2 * w], s0[8 + 2 * w + 1]);
-        pf[2][w] = T::pack(s1[2 * w], s1[2 * w + 1]);
-        pf[3][w] = T::pack(s1[8 + 2 * w], s1[8 + 2 * w + 1]);
-      }
+    for (int i = 0; i < D / 8; ++i) {
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+    }
+  };
+
+  // O^T += V^T P^T for one tile; the A operand comes from two transposed
+  // 8-byte reads of the V tile.
+  auto pv_tile = [&](const unsigned char* vt, const u32x4 (&pf)[4]) {
+    const unsigned char* vp = vt + vofs;
 #pragma unroll
-      for (int t = 0; t < D / 32; ++t) {
-        acc[t] *= alpha;
-        const unsigned char* vr = vt + (32 * t + n) * (kBc * 2);
+    for (int t = 0; t < D / 32; ++t) {
 #pragma unroll
-        for (int cc = 0; cc < 4; ++cc)
-          acc[t] = T::mfma(*(const u32x4*)(vr + (((2 * cc + hh) ^ (n & 7)) << 4)), pf[cc], acc[t]);
+      for (int cc = 0; cc < 4; ++cc) {
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_s16x4_t)as_lds(vp + (16 * cc) * G::kSV + 64 * t));
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_s16x4_t)as_lds(vp + (16 * cc + 4) * G::kSV + 64 * t));
+        const u32x2 l2 = __builtin_bit_cast(u32x2, lo);
+        const u32x2 h2 = __builtin_bit_cast(u32x2, hi);
+        const u32x4 a = {l2.x, l2.y, h2.x, h2.y};
+        acc[t] = T::mfma(a, pf[cc], acc[t]);
       }
     }
-    __syncthreads();
-  }
+  };
 
-  const float l_tot = wave_pair_sum(l_run);
+  // Sets the scores of keys a row may not see (later than the row when
+  // causal, or past the end of the sequence) to -inf. Register r of sc0
+  // holds key kbase + 8*hh + kc(r) with kc(r) = sigma(acc_row(r, 0)); sc1
+  // adds 32; a key is visible iff its kc <= lim.
+  auto mask_tile = [&](int kbase) {
+    const int last = CAUSAL ? min(qrow, N - 1) : N - 1;
+    const int lim = last - kbase - 8 * hh;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int kc = 16 * (r >> 3) + 4 * ((r >> 2) & 1) + (r & 3);
+      sc0[r] = kc <= lim ? sc0[r] : -INFINITY;
+      sc1[r] = kc + 32 <= lim ? sc1[r] : -INFINITY;
+    }
+  };
+
+  // Online-softmax step for the tile held in sc0/sc1: row max (c > 0, so
+  // max(S) c == max(S c)), a possible move of the exponent reference,
+  // P = exp2(S c - m) packed to the input type, and the row sum of the
+  // unrounded P. Returns alpha, the factor the output accumulator must take
+  // (1 unless `moved`).
+  auto softmax = [&](u32x4 (&pf)[4], bool& moved) {
+    float mx = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, fmaxf(sc0[r], sc1[r]));
+    mx = pair_max(mx);
+    const float mxs = mx == -INFINITY ? -INFINITY : mx * c;
+    moved = __builtin_amdgcn_ballot_w64(mxs > m_run + kTau) != 0;
+    const float m_new = moved ? fmaxf(m_run, mxs) : m_run;
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    m_run = m_new;
+    const float negm = -m_new;
+    float ls = 0.f;
+    // P in pack order: chunk cc of pf holds registers 8*(cc&1) .. +7 of
+    // sc0 (cc < 2) or sc1; each pair is exponentiated, summed and packed at
+    // once so the fp32 values die early.
+#pragma unroll
+    for (int cc = 0; cc < 4; ++cc) {
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const int r = 8 * (cc & 1) + 2 * w;
+        const float s_lo = cc < 2 ? sc0[r] : sc1[r];
+        const float s_hi = cc < 2 ? sc0[r + 1] : sc1[r + 1];
+        const float p_lo = __builtin_amdgcn_exp2f(__builtin_fmaf(s_lo, c, negm));
+        const float p_hi = __builtin_amdgcn_exp2f(__builtin_fmaf(s_hi, c, negm));
+        ls += p_lo + p_hi;
+        pf[cc][w] = T::pack(p_lo, p_hi);
+      }
+    }
+    l_run = alpha * l_run + ls;
+    return alpha;
+  };
+
+  // Prologue: K0 and K1 in flight, then S_0.
+  issue_k(0, k0s);
+  if (nkt > 1) issue_k(1, k1s);
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  __syncthreads();
+  s_tile(k0s);
+  __builtin_amdgcn_sched_barrier(0);
+  if (nfull == 0) mask_tile(0);
+
+  // Iteration j: block 1 runs O += P_{j-1} V_{j-1} on the matrix cores while
+  // the vector ALUs turn S_j into P_j; block 2 computes S_{j+1} (and masks
+  // it if tile j+1 is diagonal or ragged). K_t lives in stage t & 1 of K,
+  // V_t in stage t & 1 of V.
+  auto iter = [&](auto par, auto haspv, int j, u32x4 (&pf_prev)[4], u32x4 (&pf_cur)[4]) {
+    constexpr int PAR = decltype(par)::value;
+    constexpr bool PV = decltype(haspv)::value;
+    unsigned char* const k_cur = PAR == 0 ? k0s : k1s;   // K_j: done, receives K_{j+2}
+    unsigned char* const k_next = PAR == 0 ? k1s : k0s;  // holds K_{j+1}
+    unsigned char* const v_cur = PAR == 0 ? v0s : v1s;   // receives V_j
+    unsigned char* const v_prev = PAR == 0 ? v1s : v0s;  // holds V_{j-1}
+
+    __syncthreads();
+    if (j + 2 < nkt) issue_k(j + 2, k_cur);
+    issue_v(j, v_cur);
+    __builtin_amdgcn_sched_barrier(0);
+
+    // ---- block 1
+    if constexpr (PV) pv_tile(v_prev, pf_prev);
+    bool moved;
+    const float alpha = softmax(pf_cur, moved);
+#pragma unroll
+    for (int cc = 0; cc < 4; ++cc) pin(pf_cur[cc]);
+    pin(l_run);
+    if constexpr (PV) {
+      constexpr int kValu = 160 / (D / 8) + 1;
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 4, 0);
+#pragma unroll
+      for (int i = 0; i < D / 8; ++i) {
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedValu, kValu, 0);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if (moved) {
+#pragma unroll
+      for (int t = 0; t < D / 32; ++t) acc[t] *= alpha;
+    }
+    __builtin_amdgcn_sched_barrier(0);
+
+    // ---- block 2
+    if (j + 1 < nkt) {
+      s_tile(k_next);
+      __builtin_amdgcn_sched_barrier(0);
+      if (j + 1 >= nfull) mask_tile((j + 1) * kBc);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's copies landed
+  };
+
+  using P0 = std::integral_constant<int, 0>;
+  using P1 = std::integral_constant<int, 1>;
+  u32x4 pfa[4], pfb[4];
+  iter(P0{}, std::false_type{}, 0, pfb, pfa);  // P_0 -> pfa
+  int j = 1;
+  for (; j + 1 < nkt; j += 2) {
+    iter(P1{}, std::true_type{}, j, pfa, pfb);      // P_j -> pfb
+    iter(P0{}, std::true_type{}, j + 1, pfb, pfa);  // P_{j+1} -> pfa
+  }
+  if (j < nkt) {
+    iter(P1{}, std::true_type{}, j, pfa, pfb);
+#pragma unroll
+    for (int cc = 0; cc < 4; ++cc) pfa[cc] = pfb[cc];
+  }
+  // Last PV: V_{nkt-1} was copied during the last iteration.
+  __syncthreads();
+  pv_tile((nkt - 1) & 1 ? v1s : v0s, pfa);
+
+  const float l_tot = pair_sum(l_run);
   const float inv = 1.0f / l_tot;
   if (qrow < N) {
     uint16_t* orow = O + (size_t)qrow * D;
