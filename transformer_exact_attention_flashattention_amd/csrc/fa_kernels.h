@@ -190,23 +190,25 @@ struct Geo16 {
   static constexpr int kRowB = 2 * D;         // bytes of one K/V row in memory
   static constexpr int kSK = kRowB + 16;      // LDS K row stride
   static constexpr int kSV = kRowB + 64;      // LDS V row stride
-  static constexpr int kKT = kBc * kSK;       // LDS bytes of a K tile
-  static constexpr int kVT = kBc * kSV;       // LDS bytes of a V tile
-  static constexpr int kKI = kKT / 1024;      // 1 KiB copy instructions per K tile
-  static constexpr int kVI = kVT / 1024;
-  static constexpr int kKPW = (kKI + 3) / 4;  // per wave (upper bound)
-  static constexpr int kVPW = (kVI + 3) / 4;
-  static_assert(kKT % 1024 == 0 && kVT % 1024 == 0, "tiles are whole copy blocks");
+  // LDS bytes of a K (V) tile, rounded up to whole 4 KiB so that each of the
+  // 4 waves issues the same number of 1 KiB copies; slots past the 64 rows
+  // are filler nobody reads.
+  static constexpr int kKT = (kBc * kSK + 4095) / 4096 * 4096;
+  static constexpr int kVT = (kBc * kSV + 4095) / 4096 * 4096;
+  static constexpr int kKPW = kKT / 4096;     // 1 KiB copies per wave per K tile
+  static constexpr int kVPW = kVT / 4096;
 };
 
 // Source byte offset (relative to the tile's first row) of LDS slot t of a
-// tile whose rows are `stride` bytes apart.
+// tile whose rows are STRIDE bytes apart: pad slots and filler past the 64
+// rows fetch a real chunk again (their LDS bytes are never read).
 template <int D, int STRIDE>
 __device__ __forceinline__ uint32_t tile_src(int t) {
   constexpr int R = STRIDE / 16;  // 16-byte slots per LDS row
   const int m = t / R;
   int q = t - m * R;
   if (q >= D / 8) q = 0;  // pad slot
+  if (m >= kBc) return 0;  // filler
   return (uint32_t)(m * 2 * D + 16 * q);
 }
 
@@ -250,37 +252,35 @@ constexpr uint32_t kBufWord3 = 0x00020000u;  // raw buffer, 32-bit data format
 
 // Copies one tile (its first row at `src`, `nvalid` rows of the sequence
 // left from there) into LDS at `dst`: wave w issues copy blocks w, w + 4, ...
-// of the NBLK 1 KiB blocks; off[i] is the lane's source offset for its i-th
-// block. In a ragged tile, rows past the end re-fetch the last real row.
-template <int D, int NBLK>
+// of the 1 KiB blocks; off[i] is the lane's source offset for its i-th
+// block. The buffer's range is the tile's valid rows, so in a ragged last
+// tile the lanes past the end load zeros. No branches: the copies can be
+// interleaved with matrix-core work.
+template <int D, int NPW>
 __device__ __forceinline__ void copy_tile(const unsigned char* src, int nvalid, unsigned char* dst,
-                                          const uint32_t (&off)[(NBLK + 3) / 4], int wave) {
+                                          const uint32_t (&off)[NPW], int wave) {
 #if defined(__HIP_DEVICE_COMPILE__)  // buffer resources exist only on the device side
-  constexpr int kRowB = 2 * D;
+  const int rows = nvalid < kBc ? nvalid : kBc;
   const __amdgpu_buffer_rsrc_t rs =
-      __builtin_amdgcn_make_buffer_rsrc((void*)src, (short)0, kBc * kRowB, kBufWord3);
-  if (nvalid >= kBc) {
+      __builtin_amdgcn_make_buffer_rsrc((void*)src, (short)0, rows * 2 * D, kBufWord3);
 #pragma unroll
-    for (int i = 0; i < (NBLK + 3) / 4; ++i)
-      if (wave + 4 * i < NBLK)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, as_lds(dst + 1024 * (wave + 4 * i)), 16, off[i], 0, 0, 0);
-  } else {
-    const uint32_t row_end = (uint32_t)nvalid * kRowB;
-    const uint32_t last_row = row_end - kRowB;
-#pragma unroll
-    for (int i = 0; i < (NBLK + 3) / 4; ++i)
-      if (wave + 4 * i < NBLK) {
-        const uint32_t o = off[i] >= row_end ? last_row + (off[i] & (kRowB - 1)) : off[i];
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, as_lds(dst + 1024 * (wave + 4 * i)), 16, o, 0, 0, 0);
-      }
-  }
+  for (int i = 0; i < NPW; ++i)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, as_lds(dst + 1024 * (wave + 4 * i)), 16, off[i], 0, 0, 0);
 #endif
+}
+
+// s_waitcnt vmcnt(X) for a compile-time X (lgkmcnt and expcnt not waited on).
+template <int X>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(X >= 0 && X < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt((X & 15) | ((X >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
 // Scheduling masks of __builtin_amdgcn_sched_group_barrier.
 constexpr int kSchedValu = 0x0002 | 0x0400;  // VALU and transcendental
 constexpr int kSchedMfma = 0x0008;
 constexpr int kSchedDsRead = 0x0100;
+constexpr int kSchedVmem = 0x0020;  // vector memory reads
 
 template <class T, int D, bool CAUSAL>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
@@ -337,11 +337,27 @@ void fwd16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K
 #pragma unroll
   for (int i = 0; i < G::kVPW; ++i) voff[i] = tile_src<D, G::kSV>(64 * (wave + 4 * i) + lane);
 
+  // With a ragged last tile, the copy of its rows past the end may leave old
+  // LDS contents in place; starting from zeros keeps every value read finite
+  // (those keys are masked, so their values only ever meet P = 0).
+  if (N % kBc != 0) {
+    const u32x4 z = {0, 0, 0, 0};
+    for (int i = tid; i < G::kKT / 16; i += kThreads) {
+      ((u32x4*)k0s)[i] = z;
+      ((u32x4*)k1s)[i] = z;
+    }
+    for (int i = tid; i < G::kVT / 16; i += kThreads) {
+      ((u32x4*)v0s)[i] = z;
+      ((u32x4*)v1s)[i] = z;
+    }
+    __syncthreads();
+  }
+
   auto issue_k = [&](int kt, unsigned char* dst) {
-    copy_tile<D, G::kKI>(kg + (size_t)kt * kBc * G::kRowB, N - kt * kBc, dst, koff, wave);
+    copy_tile<D, G::kKPW>(kg + (size_t)kt * kBc * G::kRowB, N - kt * kBc, dst, koff, wave);
   };
   auto issue_v = [&](int kt, unsigned char* dst) {
-    copy_tile<D, G::kVI>(vg + (size_t)kt * kBc * G::kRowB, N - kt * kBc, dst, voff, wave);
+    copy_tile<D, G::kVPW>(vg + (size_t)kt * kBc * G::kRowB, N - kt * kBc, dst, voff, wave);
   };
 
   // Per-lane LDS read bases. K: MFMA row n holds key sigma(n) (second tile:
@@ -359,7 +375,8 @@ void fwd16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K
 
   // S_t = K_t Q^T into sc0 (keys 0..31 of the tile) and sc1 (keys 32..63):
   // 4 K reads ahead, then one MFMA and one read in turn.
-  auto s_tile = [&](const unsigned char* ks) {
+  auto s_tile = [&](const unsigned char* ks, auto nvmem) {
+    constexpr int NVMEM = decltype(nvmem)::value;
     sc0 = f32x16{};
     sc1 = f32x16{};
     const unsigned char* kp = ks + kofs;
@@ -368,11 +385,13 @@ void fwd16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K
       sc0 = T::mfma(*(const u32x4*)(kp + 32 * s), qf[s], sc0);
       sc1 = T::mfma(*(const u32x4*)(kp + 32 * G::kSK + 32 * s), qf[s], sc1);
     }
-    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 4, 0);
+    constexpr int kEvery = NVMEM > 0 && (D / 8) / NVMEM > 0 ? (D / 8) / NVMEM : 1;
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 8, 0);
 #pragma unroll
     for (int i = 0; i < D / 8; ++i) {
       __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
       __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+      if (NVMEM > 0 && i % kEvery == 0) __builtin_amdgcn_sched_group_barrier(kSchedVmem, 1, 0);
     }
   };
 
@@ -380,10 +399,12 @@ void fwd16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K
   // 8-byte reads of the V tile.
   auto pv_tile = [&](const unsigned char* vt, const u32x4 (&pf)[4]) {
     const unsigned char* vp = vt + vofs;
+    // Consecutive MFMAs go to different accumulators (t inner), so none
+    // waits for the previous one's result.
 #pragma unroll
-    for (int t = 0; t < D / 32; ++t) {
+    for (int cc = 0; cc < 4; ++cc) {
 #pragma unroll
-      for (int cc = 0; cc < 4; ++cc) {
+      for (int t = 0; t < D / 32; ++t) {
         const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
             (lds_s16x4_t)as_lds(vp + (16 * cc) * G::kSV + 64 * t));
         const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
@@ -448,33 +469,39 @@ void fwd16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K
     return alpha;
   };
 
-  // Prologue: K0 and K1 in flight, then S_0.
+  // Prologue: K0, K1 and V0 copied, then S_0.
   issue_k(0, k0s);
   if (nkt > 1) issue_k(1, k1s);
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  issue_v(0, v0s);
+  wait_vmcnt<0>();
   __syncthreads();
-  s_tile(k0s);
+  s_tile(k0s, std::integral_constant<int, 0>{});
   __builtin_amdgcn_sched_barrier(0);
   if (nfull == 0) mask_tile(0);
+
+  constexpr int kNK = G::kKPW, kNV = G::kVPW;  // copies per wave per tile
 
   // Iteration j: block 1 runs O += P_{j-1} V_{j-1} on the matrix cores while
   // the vector ALUs turn S_j into P_j; block 2 computes S_{j+1} (and masks
   // it if tile j+1 is diagonal or ragged). K_t lives in stage t & 1 of K,
-  // V_t in stage t & 1 of V.
+  // V_t in stage t & 1 of V. The copies of K_{j+2} are spread through block
+  // 1 and those of V_{j+1} through block 2 (issuing them in one burst stalls
+  // the wave while the vector-memory queue drains), so each copy has about
+  // an iteration and a half to land. Past the last tile the K copy re-reads
+  // the last tile into the free stage, which keeps the wait counts uniform.
   auto iter = [&](auto par, auto haspv, int j, u32x4 (&pf_prev)[4], u32x4 (&pf_cur)[4]) {
     constexpr int PAR = decltype(par)::value;
     constexpr bool PV = decltype(haspv)::value;
     unsigned char* const k_cur = PAR == 0 ? k0s : k1s;   // K_j: done, receives K_{j+2}
     unsigned char* const k_next = PAR == 0 ? k1s : k0s;  // holds K_{j+1}
-    unsigned char* const v_cur = PAR == 0 ? v0s : v1s;   // receives V_j
+    unsigned char* const v_next = PAR == 0 ? v1s : v0s;  // V_{j-1}: done mid-iteration, receives V_{j+1}
     unsigned char* const v_prev = PAR == 0 ? v1s : v0s;  // holds V_{j-1}
 
     __syncthreads();
-    if (j + 2 < nkt) issue_k(j + 2, k_cur);
-    issue_v(j, v_cur);
     __builtin_amdgcn_sched_barrier(0);
 
     // ---- block 1
+    issue_k(min(j + 2, nkt - 1), k_cur);
     if constexpr (PV) pv_tile(v_prev, pf_prev);
     bool moved;
     const float alpha = softmax(pf_cur, moved);
@@ -483,12 +510,14 @@ void fwd16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K
     pin(l_run);
     if constexpr (PV) {
       constexpr int kValu = 160 / (D / 8) + 1;
-      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 4, 0);
+      constexpr int kEvery = (D / 8) / kNK > 0 ? (D / 8) / kNK : 1;
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 8, 0);
 #pragma unroll
       for (int i = 0; i < D / 8; ++i) {
         __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
         __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
         __builtin_amdgcn_sched_group_barrier(kSchedValu, kValu, 0);
+        if (i % kEvery == 0) __builtin_amdgcn_sched_group_barrier(kSchedVmem, 1, 0);
       }
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -500,12 +529,20 @@ void fwd16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K
 
     // ---- block 2
     if (j + 1 < nkt) {
-      s_tile(k_next);
+      // K_{j+1} landed (issued before V_j and K_{j+2}), and every wave is
+      // done reading V_{j-1}.
+      wait_vmcnt<kNK + kNV>();
+      __syncthreads();
+      __builtin_amdgcn_sched_barrier(0);
+      issue_v(j + 1, v_next);
+      s_tile(k_next, std::integral_constant<int, kNV>{});
       __builtin_amdgcn_sched_barrier(0);
       if (j + 1 >= nfull) mask_tile((j + 1) * kBc);
+      // V_j landed before the next iteration reads it.
+      wait_vmcnt<kNK + kNV>();
+    } else {
+      wait_vmcnt<0>();
     }
-    __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's copies landed
   };
 
   using P0 = std::integral_constant<int, 0>;
