@@ -241,12 +241,14 @@ __device__ __forceinline__ float pair_sum(float x) {
   return __uint_as_float(p[0]) + __uint_as_float(p[1]);
 }
 
-// The running max used as the exponent reference only moves when a tile's
-// max exceeds it by more than kTau (log2 units). The result is the same in
-// exact arithmetic for any reference (the final division by the running sum
-// cancels it); skipping small moves spares the rescale of the output
-// accumulator on most tiles, at the price of P values up to 2^kTau.
+// The exponent reference m (log2 units) need not be the exact running max:
+// the result is the same in exact arithmetic for any reference (the final
+// division by the running sum cancels it), and fp32/bf16 only need the P
+// values bounded. m therefore stays put while every P of a tile is at most
+// 2^kTau, which spares both the row max and the rescale of the output
+// accumulator on most tiles; it moves to the true running max otherwise.
 constexpr float kTau = 8.0f;
+constexpr float kTauPow = 256.0f;  // 2^kTau
 
 constexpr uint32_t kBufWord3 = 0x00020000u;  // raw buffer, 32-bit data format
 
@@ -432,26 +434,13 @@ void fwd16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K
     }
   };
 
-  // Online-softmax step for the tile held in sc0/sc1: row max (c > 0, so
-  // max(S) c == max(S c)), a possible move of the exponent reference,
-  // P = exp2(S c - m) packed to the input type, and the row sum of the
-  // unrounded P. Returns alpha, the factor the output accumulator must take
-  // (1 unless `moved`).
-  auto softmax = [&](u32x4 (&pf)[4], bool& moved) {
-    float mx = -INFINITY;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, fmaxf(sc0[r], sc1[r]));
-    mx = pair_max(mx);
-    const float mxs = mx == -INFINITY ? -INFINITY : mx * c;
-    moved = __builtin_amdgcn_ballot_w64(mxs > m_run + kTau) != 0;
-    const float m_new = moved ? fmaxf(m_run, mxs) : m_run;
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-    m_run = m_new;
-    const float negm = -m_new;
-    float ls = 0.f;
-    // P in pack order: chunk cc of pf holds registers 8*(cc&1) .. +7 of
-    // sc0 (cc < 2) or sc1; each pair is exponentiated, summed and packed at
-    // once so the fp32 values die early.
+  // P = exp2(S c - m) for the tile held in sc0/sc1, packed to the input
+  // type (chunk cc of pf holds registers 8*(cc&1) .. +7 of sc0 for cc < 2,
+  // of sc1 otherwise), and the lane's sum of the unrounded P. Masked scores
+  // (-inf) give 0.
+  auto exp_tile = [&](float m, u32x4 (&pf)[4]) {
+    const float negm = -m;
+    float ls[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int cc = 0; cc < 4; ++cc) {
 #pragma unroll
@@ -461,12 +450,24 @@ void fwd16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K
         const float s_hi = cc < 2 ? sc0[r + 1] : sc1[r + 1];
         const float p_lo = __builtin_amdgcn_exp2f(__builtin_fmaf(s_lo, c, negm));
         const float p_hi = __builtin_amdgcn_exp2f(__builtin_fmaf(s_hi, c, negm));
-        ls += p_lo + p_hi;
+        ls[w] += p_lo + p_hi;
         pf[cc][w] = T::pack(p_lo, p_hi);
       }
     }
-    l_run = alpha * l_run + ls;
-    return alpha;
+    return (ls[0] + ls[1]) + (ls[2] + ls[3]);
+  };
+
+  // Row max of the tile held in sc0/sc1, scaled (c > 0, so max(S) c ==
+  // max(S c)); -inf if every key of the row is masked.
+  auto tile_max = [&]() {
+    float m0 = -INFINITY, m1 = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      m0 = fmaxf(m0, sc0[r]);
+      m1 = fmaxf(m1, sc1[r]);
+    }
+    const float mx = pair_max(fmaxf(m0, m1));
+    return mx == -INFINITY ? -INFINITY : mx * c;
   };
 
   // Prologue: K0, K1 and V0 copied, then S_0.
@@ -503,13 +504,12 @@ void fwd16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K
     // ---- block 1
     issue_k(min(j + 2, nkt - 1), k_cur);
     if constexpr (PV) pv_tile(v_prev, pf_prev);
-    bool moved;
-    const float alpha = softmax(pf_cur, moved);
+    float ls = exp_tile(m_run, pf_cur);
 #pragma unroll
     for (int cc = 0; cc < 4; ++cc) pin(pf_cur[cc]);
-    pin(l_run);
+    pin(ls);
     if constexpr (PV) {
-      constexpr int kValu = 160 / (D / 8) + 1;
+      constexpr int kValu = 110 / (D / 8) + 1;
       constexpr int kEvery = (D / 8) / kNK > 0 ? (D / 8) / kNK : 1;
       __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 8, 0);
 #pragma unroll
@@ -521,10 +521,18 @@ void fwd16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K
       }
     }
     __builtin_amdgcn_sched_barrier(0);
-    if (moved) {
+    // Some P of the tile may exceed 2^kTau (or m_run was still -inf): move
+    // the reference to the running max and redo P (rare).
+    if (__builtin_amdgcn_ballot_w64(!(ls <= kTauPow)) != 0) {
+      const float m_new = fmaxf(m_run, tile_max());
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      m_run = m_new;
+      ls = exp_tile(m_new, pf_cur);
+      l_run *= alpha;
 #pragma unroll
       for (int t = 0; t < D / 32; ++t) acc[t] *= alpha;
     }
+    l_run += ls;
     __builtin_amdgcn_sched_barrier(0);
 
     // ---- block 2
