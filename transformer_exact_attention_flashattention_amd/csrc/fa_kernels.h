@@ -278,6 +278,21 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((X & 15) | ((X >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
+// Workgroup barrier for the key loop. __syncthreads() is a release/acquire
+// fence plus s_barrier, and the fence waits for every outstanding vector
+// memory operation, LDS-bound tile copies included, so it would drain the
+// copies that are meant to stay in flight across the barrier. This barrier
+// waits only for the wave's own LDS reads (so the stage they read may be
+// overwritten once every wave has arrived); the caller waits explicitly
+// (wait_vmcnt) for the copies whose data the next phase reads. The empty
+// asm statements keep the compiler from moving memory accesses across it.
+__device__ __forceinline__ void tile_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0) only
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // Scheduling masks of __builtin_amdgcn_sched_group_barrier.
 constexpr int kSchedValu = 0x0002 | 0x0400;  // VALU and transcendental
 constexpr int kSchedMfma = 0x0008;
@@ -498,7 +513,7 @@ void fwd16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K
     unsigned char* const v_next = PAR == 0 ? v1s : v0s;  // V_{j-1}: done mid-iteration, receives V_{j+1}
     unsigned char* const v_prev = PAR == 0 ? v1s : v0s;  // holds V_{j-1}
 
-    __syncthreads();
+    tile_barrier();
     __builtin_amdgcn_sched_barrier(0);
 
     // ---- block 1
@@ -540,7 +555,7 @@ void fwd16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K
       // K_{j+1} landed (issued before V_j and K_{j+2}), and every wave is
       // done reading V_{j-1}.
       wait_vmcnt<kNK + kNV>();
-      __syncthreads();
+      tile_barrier();
       __builtin_amdgcn_sched_barrier(0);
       issue_v(j + 1, v_next);
       s_tile(k_next, std::integral_constant<int, kNV>{});
