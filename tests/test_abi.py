@@ -76,7 +76,8 @@ def test_zero_size_is_a_noop(kw):
 def test_grid_query():
     assert fa.grid(1, 16, 16384, 256, 1, 1) == (16 * 128, 128)
     assert fa.grid(2, 12, 256, 64, 0, 0) == (24 * 2, 128)
-    assert fa.grid(1, 1, 1, 64, 0, 2) == (1, 128)
+    assert fa.grid(1, 1, 1, 64, 0, 2) == (1, 64)
+    assert fa.grid(4, 1, 4096, 64, 0, 2) == (4 * 64, 64)
     with pytest.raises(fa.FaError):
         fa.grid(1, 1, 1, 80, 0, 2)
 

@@ -36,6 +36,9 @@ fwd32_fn pick32(int d, bool causal) {
   return nullptr;
 }
 
+// Query rows per workgroup of the kernel that serves dtype.
+int rows_per_block(int dtype) { return dtype == FA_F32 ? fa::kBr32 : fa::kBr; }
+
 // Checks that do not involve pointers. Fills the launch shape on success.
 int check_shape(int B, int H, int N, int d, int causal, int dtype, long long* nblocks, int* nqt) {
   if (B < 0 || H < 0 || N < 0 || d < 0) return FA_ERR_SHAPE;
@@ -44,8 +47,9 @@ int check_shape(int B, int H, int N, int d, int causal, int dtype, long long* nb
   if (causal != 0 && causal != 1) return FA_ERR_ARG;
   // Row offsets inside one head are computed in 32-bit arithmetic before
   // widening, so keep N comfortably below 2^30.
+  const int rows = rows_per_block(dtype);
   if (N > (1 << 30) - fa::kBr) return FA_ERR_SHAPE;
-  const long long q_tiles = (N + fa::kBr - 1) / fa::kBr;
+  const long long q_tiles = (N + rows - 1) / rows;
   const long long blocks = (long long)B * (long long)H * q_tiles;
   if (blocks > INT_MAX) return FA_ERR_SHAPE;
   *nblocks = blocks;
@@ -81,7 +85,7 @@ extern "C" int fa_fwd_grid(int B, int H, int N, int d, int causal, int dtype, lo
   const int st = check_shape(B, H, N, d, causal, dtype, &nblocks, &nqt);
   if (st != FA_OK) return st;
   if (workgroups) *workgroups = nblocks;
-  if (rows_per_workgroup) *rows_per_workgroup = fa::kBr;
+  if (rows_per_workgroup) *rows_per_workgroup = rows_per_block(dtype);
   return FA_OK;
 }
 

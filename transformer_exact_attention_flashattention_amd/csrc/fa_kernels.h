@@ -115,27 +115,25 @@ __device__ __forceinline__ void decode_block(int nblocks, int nqt, bool causal, 
   if (causal) qt = nqt - 1 - qt;
 }
 
-// One online-softmax update for the 32 scores a lane holds (two 16-value
-// MFMA tiles s0, s1 covering keys kbase + [0, 64) of query row qrow).
-// On return s0/s1 hold P = exp2(S*c - m_new), unrounded fp32; returns alpha.
+// One online-softmax update for the 16 scores a lane holds: the 32x32 MFMA
+// tile s of keys kb + [0, 32) (register r: key kb + acc_row(r, hh)) for query
+// row qrow. Every row of the tile sees at least one key (the caller skips a
+// tile whose first key is past the rows or the sequence), so the new max is
+// finite. On return s holds P = exp2(S*c - m_new), unrounded fp32; returns
+// alpha = exp2(m_old - m_new).
 template <bool CAUSAL>
-__device__ __forceinline__ float online_softmax(f32x16& s0, f32x16& s1, float c, int kbase, int qrow,
-                                                int q0, int N, int hh, int kperm_mask,
-                                                float& m_run, float& l_run) {
-  const bool need_mask = (CAUSAL && kbase + kBc - 1 > q0) || (kbase + kBc > N);
+__device__ __forceinline__ float online_softmax(f32x16& s, float c, int kb, int qrow, int q0, int N,
+                                                int hh, float& m_run, float& l_run) {
+  const bool need_mask = (CAUSAL && kb + 31 > q0) || (kb + 32 > N);
   float mx = -INFINITY;
   if (need_mask || c < 0.f) {
     // Scaled path: t = S * c for visible keys, -inf for masked ones.
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      int kr = acc_row(r, hh);
-      int key0 = kbase + (kperm_mask ? sigma(kr) : kr);
-      int key1 = key0 + 32;
-      bool ok0 = key0 < N && (!CAUSAL || key0 <= qrow);
-      bool ok1 = key1 < N && (!CAUSAL || key1 <= qrow);
-      s0[r] = ok0 ? s0[r] * c : -INFINITY;
-      s1[r] = ok1 ? s1[r] * c : -INFINITY;
-      mx = fmaxf(mx, fmaxf(s0[r], s1[r]));
+      const int key = kb + acc_row(r, hh);
+      const bool ok = key < N && (!CAUSAL || key <= qrow);
+      s[r] = ok ? s[r] * c : -INFINITY;
+      mx = fmaxf(mx, s[r]);
     }
     mx = wave_pair_max(mx);
     const float m_new = fmaxf(m_run, mx);
@@ -143,9 +141,8 @@ __device__ __forceinline__ float online_softmax(f32x16& s0, f32x16& s1, float c,
     float ls = 0.f;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      s0[r] = __builtin_amdgcn_exp2f(s0[r] - m_new);
-      s1[r] = __builtin_amdgcn_exp2f(s1[r] - m_new);
-      ls += s0[r] + s1[r];
+      s[r] = __builtin_amdgcn_exp2f(s[r] - m_new);
+      ls += s[r];
     }
     l_run = alpha * l_run + ls;
     m_run = m_new;
@@ -153,16 +150,15 @@ __device__ __forceinline__ float online_softmax(f32x16& s0, f32x16& s1, float c,
   }
   // Fast path (no masked key, c >= 0): max(S) * c == max(S * c).
 #pragma unroll
-  for (int r = 0; r < 16; ++r) mx = fmaxf(mx, fmaxf(s0[r], s1[r]));
+  for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[r]);
   mx = wave_pair_max(mx) * c;
   const float m_new = fmaxf(m_run, mx);
   const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
   float ls = 0.f;
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
-    s0[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s0[r], c, -m_new));
-    s1[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s1[r], c, -m_new));
-    ls += s0[r] + s1[r];
+    s[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -m_new));
+    ls += s[r];
   }
   l_run = alpha * l_run + ls;
   m_run = m_new;
@@ -606,9 +602,18 @@ void fwd16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K
 
 // ---------------------------------------------------------------------------
 // fp32 kernel (v_mfma_f32_32x32x2_f32; P stays fp32).
+//
+// 64 query rows per workgroup, so that a small batch of long sequences
+// still gives every compute unit a workgroup. Wave w owns rows 32*(w & 1) ..
+// +31 and the key half h = w >> 1 of every 64-key tile (keys 32h .. 32h+31):
+// the two waves of a row block run the online softmax over disjoint key
+// sets, and at the end the h = 1 wave hands its (m, l, O) to the h = 0 wave
+// through LDS, which merges them with the same rescaling rule.
 // LDS: ks = K tile [64][D] floats with the 16-byte chunk swizzle ch ^ (m & 7)
 // (no key permutation); vs = V tile [64][D + 8] floats, rows padded by 32
 // bytes so the two lane halves (keys 4 apart) land on different banks.
+constexpr int kBr32 = 64;  // query rows per fp32 workgroup
+
 template <int D, bool CAUSAL>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
                           amdgpu_waves_per_eu(1, 1)))
@@ -621,6 +626,9 @@ void fwd32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
   constexpr int VS_BYTES = kBc * VSTRIDE * 4;
   constexpr int CH = kBc * DCH / kThreads;    // chunks per thread, per tensor
   constexpr bool PF = D <= 128;               // keep the next tile in VGPRs
+  // The merge area (after the loop): per row block, the h = 1 wave's
+  // accumulator (D/32 x 16 floats per lane) in ks, its m and l in vs.
+  static_assert(2 * D * 32 * 4 <= KS_BYTES && 2 * 2 * 64 * 4 <= VS_BYTES, "merge area");
 
   __shared__ __attribute__((aligned(16))) unsigned char smem[KS_BYTES + VS_BYTES];
   unsigned char* const ks = smem;
@@ -637,10 +645,12 @@ void fwd32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int rb = wave & 1;   // row block
+  const int kh = wave >> 1;  // key half of each tile
   const int n = lane & 31;
   const int hh = lane >> 5;
-  const int q0 = qt * kBr + wave * 32;
+  const int q0 = qt * kBr32 + rb * 32;
   const int qrow = q0 + n;
 
   // Q^T operands: k-steps 4u + j use d = 8u + 4hh + j.
@@ -650,7 +660,7 @@ void fwd32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
     qf[u] = qrow < N ? *(const f32x4*)(Q + (size_t)qrow * D + 8 * u + 4 * hh) : f32x4{0, 0, 0, 0};
 
   const int nkt_all = (N + kBc - 1) / kBc;
-  const int nkt = CAUSAL ? min(nkt_all, (qt * kBr + kBr - 1) / kBc + 1) : nkt_all;
+  const int nkt = CAUSAL ? min(nkt_all, (qt * kBr32 + kBr32 - 1) / kBc + 1) : nkt_all;
 
   f32x4 kreg[PF ? CH : 1], vreg[PF ? CH : 1];
 
@@ -701,36 +711,59 @@ void fwd32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
     if constexpr (PF) {
       if (kt + 1 < nkt) gload(kt + 1);
     }
-    const int kbase = kt * kBc;
-    if (!CAUSAL || kbase <= q0 + 31) {
-      f32x16 s0 = {}, s1 = {};
-      const unsigned char* kr0 = ks + n * (D * 4);
-      const unsigned char* kr1 = ks + (32 + n) * (D * 4);
+    // This wave's keys: kb .. kb + 31. A tile whose first key is past every
+    // row of the block (causal) or past the sequence is skipped; otherwise
+    // every row sees at least key kb (kb and q0 are multiples of 32).
+    const int kb = kt * kBc + 32 * kh;
+    if ((!CAUSAL || kb <= q0 + 31) && kb < N) {
+      f32x16 s = {};
+      const int krow = 32 * kh + n;
+      const unsigned char* kr = ks + krow * (D * 4);
 #pragma unroll
       for (int u = 0; u < D / 8; ++u) {
-        const int off = ((2 * u + hh) ^ (n & 7)) << 4;
-        const f32x4 a0 = *(const f32x4*)(kr0 + off);
-        const f32x4 a1 = *(const f32x4*)(kr1 + off);
+        const f32x4 a = *(const f32x4*)(kr + (((2 * u + hh) ^ (krow & 7)) << 4));
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          s0 = __builtin_amdgcn_mfma_f32_32x32x2f32(a0[j], qf[u][j], s0, 0, 0, 0);
-          s1 = __builtin_amdgcn_mfma_f32_32x32x2f32(a1[j], qf[u][j], s1, 0, 0, 0);
-        }
+        for (int j = 0; j < 4; ++j) s = __builtin_amdgcn_mfma_f32_32x32x2f32(a[j], qf[u][j], s, 0, 0, 0);
       }
-      const float alpha = online_softmax<CAUSAL>(s0, s1, c, kbase, qrow, q0, N, hh, 0, m_run, l_run);
+      const float alpha = online_softmax<CAUSAL>(s, c, kb, qrow, q0, N, hh, m_run, l_run);
 #pragma unroll
       for (int t = 0; t < D / 32; ++t) acc[t] *= alpha;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int key = acc_row(r, hh);
+        const int key = 32 * kh + acc_row(r, hh);
 #pragma unroll
-        for (int t = 0; t < D / 32; ++t) {
-          acc[t] = __builtin_amdgcn_mfma_f32_32x32x2f32(vs[key * VSTRIDE + 32 * t + n], s0[r], acc[t], 0, 0, 0);
-          acc[t] = __builtin_amdgcn_mfma_f32_32x32x2f32(vs[(key + 32) * VSTRIDE + 32 * t + n], s1[r], acc[t], 0, 0, 0);
-        }
+        for (int t = 0; t < D / 32; ++t)
+          acc[t] = __builtin_amdgcn_mfma_f32_32x32x2f32(vs[key * VSTRIDE + 32 * t + n], s[r], acc[t], 0, 0, 0);
       }
     }
     __syncthreads();
+  }
+
+  // Merge the two key halves of each row block: lane l of the h = 1 wave
+  // holds the same rows and output columns as lane l of the h = 0 wave.
+  float* const xo = (float*)ks + rb * (D * 32);  // D/32 x 16 values x 64 lanes
+  float* const xm = vs + rb * 128;               // m, then l, per lane
+  if (kh == 1) {
+#pragma unroll
+    for (int t = 0; t < D / 32; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) xo[(t * 16 + r) * 64 + lane] = acc[t][r];
+    xm[lane] = m_run;
+    xm[64 + lane] = l_run;
+  }
+  __syncthreads();
+  if (kh == 1) return;
+  {
+    const float m1 = xm[lane], l1 = xm[64 + lane];
+    const float m = fmaxf(m_run, m1);  // m_run is finite: this wave always sees key 0 of tile 0
+    const float a0 = __builtin_amdgcn_exp2f(m_run - m);
+    const float a1 = m1 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m1 - m);
+#pragma unroll
+    for (int t = 0; t < D / 32; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[t][r] = a0 * acc[t][r] + a1 * xo[(t * 16 + r) * 64 + lane];
+    l_run = a0 * l_run + a1 * l1;
+    m_run = m;
   }
 
   const float l_tot = wave_pair_sum(l_run);
