@@ -28,6 +28,8 @@ METRIC = "attention fwd TFLOPS at N=2k-16k fp16/bf16; % of MI355X MFMA peak"
 PEAK_BF16_TFLOPS = 2516.6  # MI355X dense bf16/fp16 MFMA, published
 PRIMARY = 5                # long-sequence causal d=256 workload
 SECONDARY = 4              # GPT-3-shaped causal d=128 workload (reported beside)
+FP32 = 3                   # fp32-input workload (reported beside, against the fp32 matrix peak)
+PEAK_FP32_TFLOPS = 157.3   # MI355X dense fp32 MFMA, published
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fwd16_bf16_d256_causal_n16384_traffic.json")
 
 
@@ -222,6 +224,16 @@ def main():
                             "kernel_ms_mean": round(k4, 4), "tflops": round(a4, 2),
                             "frac": round(a4 / PEAK_BF16_TFLOPS, 4), "parity_ok": par4["ok"],
                             "max_abs_dO": par4["err_o"], "max_abs_dLSE": par4["err_l"]}
+    if not args.no_secondary:
+        rows3 = np.unique(np.concatenate([np.arange(64), np.random.default_rng(1).choice(4096, 64, replace=False),
+                                          np.arange(4096 - 32, 4096)]))
+        c3, _, par3, wall3, per3 = run_config(FP32, max(args.steps, 20), args.warmup, rows3)
+        k3 = float(np.mean(per3))
+        a3 = metric_flops(c3) / (k3 * 1e-3) / 1e12
+        out["fp32"] = {"workload": "fp32-long", "B": 4, "H": 1, "N": 4096, "d": 64, "causal": False,
+                       "kernel_ms_mean": round(k3, 4), "tflops": round(a3, 2), "peak": PEAK_FP32_TFLOPS,
+                       "frac": round(a3 / PEAK_FP32_TFLOPS, 4), "parity_ok": par3["ok"],
+                       "max_abs_dO": par3["err_o"], "max_abs_dLSE": par3["err_l"]}
     if args.calibrate_copy:
         log("[bench] copy calibration: 3 x 1 GiB device-to-device copy")
         src = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
@@ -234,7 +246,8 @@ def main():
         log(f"[bench] CPU baseline: fp64 oracle on {args.cpu_heads} head(s)")
         out["cpu_baseline"] = cpu_baseline(q, k, v, scale, True, args.cpu_heads)
     print(json.dumps(out), flush=True)
-    if par["ok"] is False:
+    failed = [par["ok"]] + [out[k]["parity_ok"] for k in ("secondary", "fp32") if k in out]
+    if any(f is False for f in failed):
         sys.exit(1)
 
 

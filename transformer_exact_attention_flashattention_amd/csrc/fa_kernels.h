@@ -15,9 +15,9 @@
 // (intelliparadigm.com); all of it is fused into one kernel (its section 9.2).
 //
 // gfx950 design (not the pages' design, which targets other hardware):
-//  * one workgroup of 4 waves per (batch*head, 128-row query tile); each
-//    wave owns 32 query rows, held as MFMA B operands in VGPRs for the
-//    whole key loop;
+//  * one workgroup of 4 waves per (batch*head, 128-row query tile) for
+//    16-bit inputs (64 rows for fp32); each wave owns 32 query rows, held as
+//    MFMA B operands in registers for the whole key loop;
 //  * the kernel computes S^T = K Q^T with v_mfma_f32_32x32x16_{bf16,f16}
 //    (v_mfma_f32_32x32x2_f32 for fp32), so each lane holds one query column
 //    and 16 keys: the row max needs one exchange with lane l^32 and the row
@@ -27,13 +27,12 @@
 //    already the B-operand layout of the second MFMA, provided the K tile's
 //    rows are stored in LDS with bits 2 and 3 of the key index swapped
 //    (sigma below), which makes each lane's eight keys contiguous in V^T;
-//  * K/V tiles of 64 keys are staged global -> VGPR -> LDS, the next tile's
-//    global loads in flight while the current tile is consumed; K keeps its
-//    [key][d] rows, V is transposed to [d][key] on the LDS write; both use a
-//    16-byte-chunk XOR swizzle so 8-lane read phases hit distinct banks;
-//  * causal: key tiles past the workgroup's last row are never loaded, a
-//    wave skips tiles past its own last row, and only diagonal or ragged
-//    tiles pay for the element mask.
+//  * 16-bit K/V tiles of 64 keys go global -> LDS by buffer loads that write
+//    LDS directly, two stages each, with padded rows; V is read transposed
+//    from its natural layout by ds_read_b64_tr_b16 (fp32 tiles go through
+//    registers);
+//  * causal: key tiles past the workgroup's last row are never loaded, and
+//    only diagonal or ragged tiles pay for the element mask.
 #pragma once
 
 #include <hip/hip_runtime.h>
