@@ -18,7 +18,7 @@ Sources (the web pages this work is built from):
   section 2 (softmax of the scaled product times V).
 * [P1] "Compiling Flash Attention 2.8.3 on Windows with an RTX 3090"
   (intelliparadigm.com): section 5.2 / 10.1 (``softmax_scale=None`` means
-  1/sqrt(d); ``causal`` flag).
+  1/sqrt(d); ``causal`` flag; ``window_size`` local-attention window).
 
 Parity status: every public function here is pinned by CPU tests (brute force
 in 40-digit decimal arithmetic, closed forms, invariants, a hand-derived
@@ -26,6 +26,7 @@ fixture and a library cross-check); none is "parity unpinned".
 """
 
 from .attention import (  # noqa: F401
+    allowed_ref,
     attention_ref,
     attention_tiled_ref,
     scores_ref,

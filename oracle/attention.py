@@ -16,6 +16,12 @@ Readings of the pages used here (where they are silent or disagree):
   lengths are equal, so every row keeps at least its diagonal key.
 * LSE_i = ln sum_j exp(S_ij) over allowed j, in natural log (the pages never
   write it; it is the row statistic m + ln l of the online recurrence).
+* window = (left, right) is the local-attention window that [P1] 10.1 lists
+  as ``window_size=(-1, -1)`` without defining it: key j is allowed for query
+  i iff j >= i - left (when left >= 0) and j <= i + right (when right >= 0);
+  -1 leaves that side unbounded, so (-1, -1) is full attention. It combines
+  with causal by intersection. The diagonal key is always allowed, so no row
+  is empty.
 """
 
 from __future__ import annotations
@@ -35,23 +41,49 @@ def _check(q, k, v):
         raise ValueError(f"q, k, v must share one [B,H,N,d] shape: {q.shape} {k.shape} {v.shape}")
 
 
-def scores_ref(q_bh, k_bh, scale, causal, rows=None):
+def _check_window(window):
+    left, right = (int(w) for w in window)
+    if left < -1 or right < -1:
+        raise ValueError(f"window sides must be >= -1 (-1: unbounded), got {window}")
+    return left, right
+
+
+def allowed_ref(rows, keys, causal, window=(-1, -1)):
+    """Boolean [len(rows), len(keys)]: may query row i attend to key j?
+
+    causal: j <= i ([P3] 1.1 lower-triangular mask). window (left, right):
+    j >= i - left and j <= i + right, each side only when >= 0 (the reading
+    of [P1] 10.1 ``window_size`` stated in the module docstring).
+    """
+    left, right = _check_window(window)
+    i = np.asarray(rows, dtype=np.int64)[:, None]
+    j = np.asarray(keys, dtype=np.int64)[None, :]
+    ok = np.ones((i.shape[0], j.shape[1]), dtype=bool)
+    if causal:
+        ok &= j <= i
+    if left >= 0:
+        ok &= j >= i - left
+    if right >= 0:
+        ok &= j <= i + right
+    return ok
+
+
+def scores_ref(q_bh, k_bh, scale, causal, rows=None, window=(-1, -1)):
     """S = scale * Q K^T for one (batch, head), masked entries set to -inf.
 
     Step 1 of standard attention ([P3] 1.1, [P2] 2, [P5] standard_attention):
-    S_ij = scale * sum_c Q_ic K_jc. With ``causal`` the entries with j > i are
-    filled with -inf ([P3] 1.1 ``masked_fill``). ``rows`` selects query rows
-    (default: all); the returned S has one row per selected query and one
-    column per key.
+    S_ij = scale * sum_c Q_ic K_jc. Entries a row may not attend to (causal:
+    j > i; outside the window) are filled with -inf ([P3] 1.1
+    ``masked_fill``). ``rows`` selects query rows (default: all); the
+    returned S has one row per selected query and one column per key.
     """
     q_bh = _f64(q_bh)
     k_bh = _f64(k_bh)
     n = k_bh.shape[0]
     rows = np.arange(q_bh.shape[0]) if rows is None else np.asarray(rows, dtype=np.int64)
     s = float(scale) * (q_bh[rows] @ k_bh.T)
-    if causal:
-        keys = np.arange(n)
-        s = np.where(keys[None, :] > rows[:, None], -np.inf, s)
+    if causal or tuple(window) != (-1, -1):
+        s = np.where(allowed_ref(rows, np.arange(n), causal, window), s, -np.inf)
     return s
 
 
@@ -67,7 +99,7 @@ def softmax_rows_ref(s):
     return e / l, m[:, 0], l[:, 0]
 
 
-def attention_ref(q, k, v, scale, causal=False, rows=None, chunk=1024):
+def attention_ref(q, k, v, scale, causal=False, rows=None, chunk=1024, window=(-1, -1)):
     """Plain three-step attention: O = softmax(scale Q K^T [+ mask]) V, and LSE.
 
     [P3] 1.1 (QK^T, mask + softmax, times V), [P2] 2 and [P5]
@@ -88,14 +120,14 @@ def attention_ref(q, k, v, scale, causal=False, rows=None, chunk=1024):
         for h in range(H):
             for c0 in range(0, R, chunk):
                 rr = rows[c0:c0 + chunk]
-                s = scores_ref(q[b, h], k[b, h], scale, causal, rr)
+                s = scores_ref(q[b, h], k[b, h], scale, causal, rr, window)
                 p, m, l = softmax_rows_ref(s)
                 out[b, h, c0:c0 + chunk] = p @ v[b, h]
                 lse[b, h, c0:c0 + chunk] = m + np.log(l)
     return out, lse
 
 
-def attention_tiled_ref(q, k, v, scale, causal=False, Br=64, Bc=64):
+def attention_tiled_ref(q, k, v, scale, causal=False, Br=64, Bc=64, window=(-1, -1)):
     """Tiled forward with the online-softmax recurrence, in float64.
 
     Follows [P5] ``flash_attention_forward``: for each block of Br query rows,
@@ -109,7 +141,9 @@ def attention_tiled_ref(q, k, v, scale, causal=False, Br=64, Bc=64):
     One addition the page does not need (it has no mask): while every key a
     row has seen so far is masked, m_new stays -inf and exp(-inf - (-inf))
     would be NaN, so such rows keep their state (c = 1, P = 0) for that
-    block. The LSE of a row is m + ln l after the last block.
+    block. The LSE of a row is m + ln l after the last block. ``window`` as
+    in ``attention_ref``; with it a row's first blocks can be fully masked,
+    which the same guard covers.
     """
     q, k, v = _f64(q), _f64(k), _f64(v)
     _check(q, k, v)
@@ -127,8 +161,8 @@ def attention_tiled_ref(q, k, v, scale, causal=False, Br=64, Bc=64):
                 for ks in range(0, N, Bc):
                     ke = min(ks + Bc, N)
                     s = float(scale) * (qi @ k[b, h, ks:ke].T)
-                    if causal:
-                        allowed = np.arange(ks, ke)[None, :] <= np.arange(qs, qe)[:, None]
+                    if causal or tuple(window) != (-1, -1):
+                        allowed = allowed_ref(np.arange(qs, qe), np.arange(ks, ke), causal, window)
                         s = np.where(allowed, s, -np.inf)
                     m_new = np.maximum(m, s.max(axis=1))
                     live = np.isfinite(m_new)

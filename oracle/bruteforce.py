@@ -14,12 +14,15 @@ from decimal import Decimal, localcontext
 import numpy as np
 
 
-def attention_bruteforce(q, k, v, scale, causal=False, digits=40):
+def attention_bruteforce(q, k, v, scale, causal=False, digits=40, window=(-1, -1)):
     """Return (O, LSE) as float64 arrays, computed in Decimal at ``digits``.
 
     Every float input converts to Decimal exactly. A masked key (causal and
-    j > i) is left out of both sums, which is what a -inf score means.
+    j > i, or outside the window: j < i - left for left >= 0, j > i + right
+    for right >= 0) is left out of both sums, which is what a -inf score
+    means.
     """
+    left, right = int(window[0]), int(window[1])
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
@@ -37,6 +40,10 @@ def attention_bruteforce(q, k, v, scale, causal=False, digits=40):
                     weights = []
                     for j in range(N):
                         if causal and j > i:
+                            continue
+                        if left >= 0 and i - j > left:
+                            continue
+                        if right >= 0 and j - i > right:
                             continue
                         dot = sum((Decimal(float(q[b, h, i, c])) * Decimal(float(k[b, h, j, c]))
                                    for c in range(D)), Decimal(0))

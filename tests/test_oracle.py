@@ -308,3 +308,106 @@ def test_row_subset_matches_full():
         o_c, lse_c = attention_ref(q, k, v, 0.25, causal, chunk=7)
         np.testing.assert_allclose(o_c, o, rtol=0, atol=1e-15)
         np.testing.assert_allclose(lse_c, lse, rtol=0, atol=1e-15)
+
+
+# ------------------------------------------------- local-attention window --
+# Reading of [P1] 10.1 window_size=(left, right): key j is allowed for query
+# i iff i - left <= j <= i + right, a side of -1 unbounded; with causal the
+# two masks intersect.
+
+WINDOWS = [(0, 0), (1, 0), (0, 1), (2, 3), (3, -1), (-1, 2), (5, 5)]
+
+
+@pytest.mark.parametrize("window", WINDOWS)
+@pytest.mark.parametrize("causal", [False, True])
+def test_window_bruteforce(window, causal):
+    """The window mask against the decimal brute force, which skips keys
+    with its own comparisons."""
+    N, D = 8, 4
+    q, k, v = (rnd((1, 2, N, D), s) for s in (31, 32, 33))
+    o_bf, l_bf = attention_bruteforce(q, k, v, 0.7, causal, window=window)
+    for fn in (attention_ref, attention_tiled_ref):
+        kw = dict(Br=3, Bc=2) if fn is attention_tiled_ref else {}
+        o, lse = fn(q, k, v, 0.7, causal, window=window, **kw)
+        np.testing.assert_allclose(o, o_bf, rtol=0, atol=1e-13, err_msg=f"{fn.__name__} {window} {causal}")
+        np.testing.assert_allclose(lse, l_bf, rtol=0, atol=1e-13, err_msg=f"{fn.__name__} {window} {causal}")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_window_zero_width_is_identity(causal):
+    """window (0, 0): a row sees only its own key, so O_i = V_i exactly and
+    LSE_i = scale q_i . k_i (closed form)."""
+    N, D = 37, 8
+    q, k, v = (rnd((2, 3, N, D), s) for s in (41, 42, 43))
+    for fn in (attention_ref, attention_tiled_ref):
+        o, lse = fn(q, k, v, 0.3, causal, window=(0, 0))
+        np.testing.assert_allclose(o, v, rtol=0, atol=1e-15)
+        np.testing.assert_allclose(lse, 0.3 * np.einsum("bhnd,bhnd->bhn", q, k), rtol=0, atol=1e-13)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_window_wider_than_sequence_is_full_attention(causal):
+    """A window at least N wide on both sides masks nothing beyond causal."""
+    N, D = 50, 16
+    q, k, v = (rnd((1, 2, N, D), s) for s in (51, 52, 53))
+    o0, l0 = attention_ref(q, k, v, 0.25, causal)
+    for window in ((N, N), (N - 1, N - 1), (-1, N), (N, -1)):
+        o, lse = attention_ref(q, k, v, 0.25, causal, window=window)
+        np.testing.assert_array_equal(o, o0)
+        np.testing.assert_array_equal(lse, l0)
+
+
+def test_window_weights_vanish_outside_and_sum_to_one():
+    """With V = identity (one column per key), O is the weight matrix P: its
+    rows sum to 1 and it is exactly 0 outside the band."""
+    N = 20
+    q, k = rnd((1, 1, N, N), 61) * 0.5, rnd((1, 1, N, N), 62) * 0.5
+    v = np.eye(N)[None, None]
+    for causal in (False, True):
+        for left, right in ((2, 1), (4, -1), (-1, 3), (0, 5)):
+            p, _ = attention_ref(q, k, v, 0.9, causal, window=(left, right))
+            p = p[0, 0]
+            i, j = np.meshgrid(np.arange(N), np.arange(N), indexing="ij")
+            out = np.zeros_like(p, dtype=bool)
+            if left >= 0:
+                out |= j < i - left
+            if right >= 0:
+                out |= j > i + right
+            if causal:
+                out |= j > i
+            assert np.all(p[out] == 0.0), (left, right, causal)
+            assert np.all(p[~out] > 0.0), (left, right, causal)
+            np.testing.assert_allclose(p.sum(axis=1), 1.0, rtol=0, atol=1e-14)
+
+
+def test_window_locality():
+    """Changing keys and values outside row i's window leaves row i unchanged."""
+    N, D, i, left, right = 40, 8, 21, 3, 2
+    q, k, v = (rnd((1, 1, N, D), s) for s in (71, 72, 73))
+    o0, l0 = attention_ref(q, k, v, 0.5, False, window=(left, right))
+    k2, v2 = k.copy(), v.copy()
+    far = [j for j in range(N) if j < i - left or j > i + right]
+    k2[0, 0, far] = rnd((len(far), D), 74) * 5
+    v2[0, 0, far] = rnd((len(far), D), 75) * 5
+    o1, l1 = attention_ref(q, k2, v2, 0.5, False, window=(left, right))
+    np.testing.assert_array_equal(o1[0, 0, i], o0[0, 0, i])
+    np.testing.assert_array_equal(l1[0, 0, i], l0[0, 0, i])
+    assert not np.allclose(o1[0, 0, 0], o0[0, 0, 0])  # row 0's window does see the change
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("window", [(5, 0), (0, 7), (13, 9), (64, -1), (-1, 70), (100, 100)])
+def test_window_tiled_equals_untiled(window, causal):
+    N, D = 150, 8
+    q, k, v = (rnd((1, 2, N, D), s) for s in (81, 82, 83))
+    o0, l0 = attention_ref(q, k, v, 0.35, causal, window=window)
+    for Br, Bc in ((64, 64), (17, 23)):
+        o, lse = attention_tiled_ref(q, k, v, 0.35, causal, Br=Br, Bc=Bc, window=window)
+        np.testing.assert_allclose(o, o0, rtol=0, atol=1e-12)
+        np.testing.assert_allclose(lse, l0, rtol=0, atol=1e-12)
+
+
+def test_window_rejects_sides_below_minus_one():
+    q = rnd((1, 1, 4, 2), 91)
+    with pytest.raises(ValueError):
+        attention_ref(q, q, q, 1.0, False, window=(-2, 0))
