@@ -83,13 +83,13 @@ def time_launches(fn, stream, steps, warmup):
     return wall, per
 
 
-def check_parity(o, lse, q, k, v, scale, causal, rows):
+def check_parity(o, lse, q, k, v, scale, causal, rows, window=(-1, -1)):
     import numpy as np
 
     from oracle import attention_ref
 
     o_ref, l_ref = attention_ref(q.double().numpy(), k.double().numpy(), v.double().numpy(), scale, causal,
-                                 rows=rows)
+                                 rows=rows, window=window)
     o_g = o[:, :, rows].double().cpu().numpy()
     l_g = lse[:, :, rows].double().cpu().numpy()
     return float(np.abs(o_g - o_ref).max()), float(np.abs(l_g - l_ref).max())
@@ -153,7 +153,7 @@ def main():
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream(dev)
 
-    def run_config(cfg, steps, warmup, check_rows):
+    def run_config(cfg, steps, warmup, check_rows, window=(-1, -1)):
         c = inputs.CONFIGS[cfg]
         log(f"[bench] config {cfg} ({c['name']}): generating inputs")
         q, k, v = inputs.make_config(cfg)
@@ -163,7 +163,7 @@ def main():
         lse = torch.empty(qd.shape[:3], dtype=torch.float32, device=dev)
 
         def step():
-            fa.fwd(qd, kd, vd, softmax_scale=scale, causal=c["causal"], out=o, lse=lse)
+            fa.fwd(qd, kd, vd, softmax_scale=scale, causal=c["causal"], window_size=window, out=o, lse=lse)
 
         if args.no_parity:
             err_o = err_l = float("nan")
@@ -173,7 +173,7 @@ def main():
             o.fill_(float("nan"))
             step()
             torch.cuda.synchronize()
-            err_o, err_l = check_parity(o.cpu(), lse.cpu(), q, k, v, scale, c["causal"], check_rows)
+            err_o, err_l = check_parity(o.cpu(), lse.cpu(), q, k, v, scale, c["causal"], check_rows, window)
             tol_o = {"f16": 2e-3, "bf16": 1e-2, "f32": 1e-5}[c["dtype"]]
             ok = err_o <= tol_o and err_l <= 1e-3 and bool(torch.isfinite(o).all())
             log(f"[bench] config {cfg}: max|dO|={err_o:.3e} max|dLSE|={err_l:.3e} parity={'ok' if ok else 'FAIL'}")
@@ -234,6 +234,19 @@ def main():
                        "kernel_ms_mean": round(k3, 4), "tflops": round(a3, 2), "peak": PEAK_FP32_TFLOPS,
                        "frac": round(a3 / PEAK_FP32_TFLOPS, 4), "parity_ok": par3["ok"],
                        "max_abs_dO": par3["err_o"], "max_abs_dLSE": par3["err_l"]}
+    if not args.no_secondary:
+        # Sliding-window variant of the same workload: causal, each query sees
+        # itself and the 4096 keys before it. Flops count the visible pairs.
+        W = 4096
+        cw, _, parw, wallw, perw = run_config(PRIMARY, max(args.steps // 2, 5), 2, rows, window=(W, -1))
+        kw_ms = float(np.mean(perw))
+        pairs = sum(min(i + 1, W + 1) for i in range(cw["N"]))
+        flw = 4.0 * cw["B"] * cw["H"] * pairs * cw["D"]
+        aw = flw / (kw_ms * 1e-3) / 1e12
+        out["window"] = {"workload": "long-causal-d256, window (4096, -1)", "kernel_ms_mean": round(kw_ms, 4),
+                         "tflops": round(aw, 2), "frac": round(aw / PEAK_BF16_TFLOPS, 4),
+                         "flops_counted": "4*d per visible (query, key) pair", "parity_ok": parw["ok"],
+                         "max_abs_dO": parw["err_o"], "max_abs_dLSE": parw["err_l"]}
     if args.calibrate_copy:
         log("[bench] copy calibration: 3 x 1 GiB device-to-device copy")
         src = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
@@ -246,7 +259,7 @@ def main():
         log(f"[bench] CPU baseline: fp64 oracle on {args.cpu_heads} head(s)")
         out["cpu_baseline"] = cpu_baseline(q, k, v, scale, True, args.cpu_heads)
     print(json.dumps(out), flush=True)
-    failed = [par["ok"]] + [out[k]["parity_ok"] for k in ("secondary", "fp32") if k in out]
+    failed = [par["ok"]] + [out[k]["parity_ok"] for k in ("secondary", "fp32", "window") if k in out]
     if any(f is False for f in failed):
         sys.exit(1)
 

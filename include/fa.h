@@ -6,7 +6,8 @@
  * memory:
  *
  *   S = scale * Q K^T            (per batch b and head h)
- *   S_ij = -inf where causal and j > i (lower-triangular mask)
+ *   S_ij = -inf where causal and j > i (lower-triangular mask), or outside
+ *          the local window of fa_fwd_window
  *   O = softmax_rows(S) V,  LSE_i = ln sum_j exp(S_ij)
  *
  * Sources: the standard three-step form and its [batch, heads, seq, head_dim]
@@ -77,6 +78,25 @@ typedef enum {
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
            int B, int H, int N, int d, float scale, int causal, int dtype,
            void* stream);
+
+/*
+ * fa_fwd_window - fa_fwd with a local-attention window: query i sees key j
+ * only if i - window_left <= j <= i + window_right. A side of -1 is
+ * unbounded, so (-1, -1) is exactly fa_fwd; with causal = 1 the window and
+ * the causal mask intersect (window_right then has no effect).
+ *
+ * Source: the packed call in section 10.1 of the flash-attn 2.8.3 build
+ * guide (intelliparadigm.com) lists window_size=(-1, -1) as the local
+ * attention window without defining it; the bounds above are this library's
+ * reading of it (the same one its oracle implements). Every query row keeps
+ * its own key, so no row is empty.
+ *
+ * Arguments, layout, ownership, synchronisation and errors as fa_fwd;
+ * additionally FA_ERR_ARG if window_left or window_right is below -1.
+ */
+int fa_fwd_window(const void* q, const void* k, const void* v, void* o, float* lse,
+                  int B, int H, int N, int d, float scale, int causal,
+                  int window_left, int window_right, int dtype, void* stream);
 
 /* Static text for a status code (never NULL). */
 const char* fa_strerror(int status);

@@ -67,6 +67,32 @@ def test_validation_errors(kw, code):
     assert call(**kw) == code
 
 
+def call_window(left, right, **kw):
+    a = dict(GOOD, **kw)
+    return fa.fa_fwd_window(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["N"], a["d"],
+                            a["scale"], a["causal"], left, right, a["dtype"], None)
+
+
+@pytest.mark.parametrize("left,right", [(-2, 0), (0, -2), (-5, -5), (-(1 << 31), 3)])
+def test_window_sides_below_minus_one_rejected(left, right):
+    assert call_window(left, right) == -6
+    # checked before the zero-size early return, so also without a launch
+    assert call_window(left, right, N=0, q=0, k=0, v=0, o=0, lse=0) == -6
+
+
+@pytest.mark.parametrize("kw,code", [(dict(d=96), -3), (dict(causal=2), -6), (dict(q=0), -1)])
+def test_window_entry_shares_the_checks(kw, code):
+    assert call_window(3, 0, **kw) == code
+
+
+def test_python_window_argument_checked():
+    with pytest.raises(ValueError):
+        fa._window((-2, 0))
+    with pytest.raises(ValueError):
+        fa._window(5)
+    assert fa._window((3, -1)) == (3, -1)
+
+
 @pytest.mark.parametrize("kw", [dict(B=0), dict(H=0), dict(N=0)])
 def test_zero_size_is_a_noop(kw):
     # no launch and no pointer checks when there is nothing to compute

@@ -45,18 +45,18 @@ def np64(t):
     return t.detach().to("cpu", torch.float64).numpy()
 
 
-def run(q, k, v, scale, causal):
+def run(q, k, v, scale, causal, window=(-1, -1)):
     """q, k, v: CPU tensors. Returns CPU (o, lse) from the HIP kernels."""
     qd, kd, vd = (t.cuda() for t in (q, k, v))
     o = torch.full_like(qd, float("nan"))
     lse = torch.full(q.shape[:3], float("nan"), dtype=torch.float32, device="cuda")
-    fa.fwd(qd, kd, vd, softmax_scale=scale, causal=causal, out=o, lse=lse)
+    fa.fwd(qd, kd, vd, softmax_scale=scale, causal=causal, window_size=window, out=o, lse=lse)
     torch.cuda.synchronize()
     return o.cpu(), lse.cpu()
 
 
-def check(o, lse, q, k, v, scale, causal, rows=None, tol_o=None):
-    o_ref, lse_ref = attention_ref(np64(q), np64(k), np64(v), scale, causal, rows=rows)
+def check(o, lse, q, k, v, scale, causal, rows=None, tol_o=None, window=(-1, -1)):
+    o_ref, lse_ref = attention_ref(np64(q), np64(k), np64(v), scale, causal, rows=rows, window=window)
     o64, l64 = np64(o), np64(lse)
     if rows is not None:
         o64, l64 = o64[:, :, rows], l64[:, :, rows]
@@ -212,3 +212,55 @@ def test_python_layer_errors():
     q = torch.zeros(1, 1, 8, 64, dtype=torch.float16, device="cuda")
     with pytest.raises(ValueError):
         fa.fwd(q, q, q.transpose(2, 3))
+
+
+# ------------------------------------------------- local-attention window --
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16", "f32"])
+@pytest.mark.parametrize("D", [64, 128, 256])
+@pytest.mark.parametrize("causal", [False, True])
+def test_window_shapes(dtype, D, causal):
+    """Windows narrower than a tile, straddling tiles, one-sided and wider
+    than the sequence, on ragged lengths."""
+    for N, window in ((257, (0, 0)), (257, (5, 3)), (300, (64, 0)), (300, (70, 129)),
+                      (1000, (200, -1)), (1000, (-1, 33)), (129, (1000, 1000))):
+        q, k, v = inputs.make_qkv(1, 2, N, D, dtype, seed=N + D + window[0])
+        scale = 1.0 / math.sqrt(D)
+        o, lse = run(q, k, v, scale, causal, window)
+        check(o, lse, q, k, v, scale, causal, window=window)
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_window_zero_width_returns_v_exactly(dtype):
+    """window (0, 0): each row sees only its own key, so O = V bit for bit."""
+    q, k, v = inputs.make_qkv(2, 3, 515, 128, dtype, seed=7)
+    o, lse = run(q, k, v, 0.1, False, (0, 0))
+    assert torch.equal(o, v)
+    want = 0.1 * (q.double() * k.double()).sum(-1)
+    assert (lse.double() - want).abs().max().item() <= 1e-3
+
+
+@pytest.mark.parametrize("D,dtype", [(128, "bf16"), (256, "bf16"), (64, "f32")])
+def test_window_long_sequence_sampled_rows(D, dtype):
+    """A 4096-key causal sliding window of 512 on a long sequence: many full
+    tiles in the middle, masked tiles at both ends of each block's range."""
+    N = 8192 if dtype != "f32" else 4096
+    q, k, v = inputs.make_qkv(1, 2, N, D, dtype, seed=11)
+    rows = np.unique(np.concatenate([np.arange(200), np.arange(N // 2 - 100, N // 2 + 100), np.arange(N - 200, N)]))
+    for causal, window in ((True, (512, -1)), (False, (300, 300))):
+        o, lse = run(q, k, v, 1.0 / math.sqrt(D), causal, window)
+        check(o, lse, q, k, v, 1.0 / math.sqrt(D), causal, rows=rows, window=window)
+
+
+def test_window_minus_one_matches_plain_call():
+    """window (-1, -1) goes through the same kernels as fa_fwd: identical bits."""
+    q, k, v = inputs.make_qkv(1, 4, 777, 128, "bf16", seed=5)
+    o1, l1 = run(q, k, v, 0.09, True)
+    qd, kd, vd = (t.cuda() for t in (q, k, v))
+    o2 = torch.empty_like(qd)
+    l2 = torch.empty(q.shape[:3], dtype=torch.float32, device="cuda")
+    st = fa.fa_fwd(qd.data_ptr(), kd.data_ptr(), vd.data_ptr(), o2.data_ptr(), l2.data_ptr(), 1, 4, 777, 128,
+                   0.09, 1, fa.FA_BF16, torch.cuda.current_stream().cuda_stream)
+    assert st == 0
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2.cpu()) and torch.equal(l1, l2.cpu())

@@ -8,16 +8,20 @@ library is missing or the tensors are not on a GPU, the calls raise.
 API (names follow the flash-attn interface that section 5.2 / 10.1 of the
 flash-attn 2.8.3 build guide, intelliparadigm.com, calls):
 
-* ``fwd(q, k, v, softmax_scale=None, causal=False) -> (o, lse)`` with
-  q, k, v of shape [B, H, N, d] (the layout of section 1.1 of "2.3
-  FlashAttention and IO-aware attention"), contiguous, on one GPU, all of
-  dtype float16, bfloat16 or float32; ``softmax_scale=None`` means 1/sqrt(d).
+* ``fwd(q, k, v, softmax_scale=None, causal=False, window_size=(-1, -1))
+  -> (o, lse)`` with q, k, v of shape [B, H, N, d] (the layout of section 1.1
+  of "2.3 FlashAttention and IO-aware attention"), contiguous, on one GPU,
+  all of dtype float16, bfloat16 or float32; ``softmax_scale=None`` means
+  1/sqrt(d); ``window_size=(left, right)`` restricts query i to keys
+  i - left .. i + right (-1: unbounded side), the reading of the
+  ``window_size`` argument that section 10.1 lists.
 * ``flash_attn_qkvpacked_func(qkv, dropout_p=0.0, softmax_scale=None,
   causal=False) -> (o, lse)`` for a packed tensor [B, N, 3, H, d]; it splits
   and transposes the packed tensor into three [B, H, N, d] tensors (a copy)
   and calls ``fwd``; o and lse come back as [B, H, N, d] and [B, H, N].
-* ``fa_fwd(...)``: the raw C entry point with the same arguments as the C
-  function, for callers that manage their own pointers and streams.
+* ``fa_fwd(...)``, ``fa_fwd_window(...)``: the raw C entry points with the
+  same arguments as the C functions, for callers that manage their own
+  pointers and streams.
 """
 
 from __future__ import annotations
@@ -40,7 +44,7 @@ STATUS = {
     -7: "FA_ERR_LAUNCH",
 }
 # Every symbol include/fa.h declares.
-EXPORTS = ("fa_fwd", "fa_strerror", "fa_fwd_grid")
+EXPORTS = ("fa_fwd", "fa_fwd_window", "fa_strerror", "fa_fwd_grid")
 
 _lib = None
 
@@ -67,6 +71,12 @@ def lib() -> ctypes.CDLL:
             ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_float,
             ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
         ]
+        h.fa_fwd_window.restype = ctypes.c_int
+        h.fa_fwd_window.argtypes = [
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+            ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_float,
+            ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+        ]
         h.fa_strerror.restype = ctypes.c_char_p
         h.fa_strerror.argtypes = [ctypes.c_int]
         h.fa_fwd_grid.restype = ctypes.c_int
@@ -85,6 +95,23 @@ def strerror(status: int) -> str:
 def fa_fwd(q, k, v, o, lse, B, H, N, d, scale, causal, dtype, stream=None) -> int:
     """Raw call of the C entry point; pointers are ints (device addresses)."""
     return lib().fa_fwd(q, k, v, o, lse, B, H, N, d, scale, causal, dtype, stream)
+
+
+def fa_fwd_window(q, k, v, o, lse, B, H, N, d, scale, causal, window_left, window_right, dtype,
+                  stream=None) -> int:
+    """Raw call of the windowed C entry point; pointers are ints (device addresses)."""
+    return lib().fa_fwd_window(q, k, v, o, lse, B, H, N, d, scale, causal, window_left, window_right,
+                               dtype, stream)
+
+
+def _window(window_size):
+    try:
+        left, right = (int(w) for w in window_size)
+    except (TypeError, ValueError):
+        raise ValueError(f"window_size must be a pair of ints, got {window_size!r}") from None
+    if left < -1 or right < -1:
+        raise ValueError(f"window_size sides must be >= -1 (-1: unbounded), got {window_size!r}")
+    return left, right
 
 
 def grid(B, H, N, d, causal, dtype):
@@ -106,10 +133,11 @@ def _dtype_code(t):
     return codes[t.dtype]
 
 
-def fwd(q, k, v, softmax_scale=None, causal=False, out=None, lse=None):
+def fwd(q, k, v, softmax_scale=None, causal=False, window_size=(-1, -1), out=None, lse=None):
     """Attention forward on the GPU: returns (o [B,H,N,d], lse [B,H,N] fp32)."""
     import torch
 
+    left, right = _window(window_size)
     for name, t in (("q", q), ("k", k), ("v", v)):
         if not isinstance(t, torch.Tensor):
             raise TypeError(f"{name} must be a torch.Tensor")
@@ -140,9 +168,9 @@ def fwd(q, k, v, softmax_scale=None, causal=False, out=None, lse=None):
         raise ValueError("lse must be a contiguous float32 tensor [B, H, N] on q's device")
     with torch.cuda.device(q.device):
         stream = torch.cuda.current_stream().cuda_stream
-        st = lib().fa_fwd(
+        st = lib().fa_fwd_window(
             q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
-            B, H, N, d, scale, int(bool(causal)), code, stream,
+            B, H, N, d, scale, int(bool(causal)), left, right, code, stream,
         )
     if st != 0:
         raise FaError(st, strerror(st))
@@ -154,18 +182,16 @@ def flash_attn_qkvpacked_func(qkv, dropout_p=0.0, softmax_scale=None, causal=Fal
     """Packed-QKV entry: qkv [B, N, 3, H, d] -> (o [B,H,N,d], lse [B,H,N])."""
     if dropout_p != 0.0:
         raise NotImplementedError("dropout is not supported")
-    if tuple(window_size) != (-1, -1):
-        raise NotImplementedError("local (windowed) attention is not supported")
     if alibi_slopes is not None:
         raise NotImplementedError("ALiBi is not supported")
     if qkv.dim() != 5 or qkv.shape[2] != 3:
         raise ValueError(f"qkv must be [B, N, 3, H, d], got {tuple(qkv.shape)}")
     q, k, v = (qkv[:, :, i].permute(0, 2, 1, 3).contiguous() for i in range(3))
-    return fwd(q, k, v, softmax_scale=softmax_scale, causal=causal)
+    return fwd(q, k, v, softmax_scale=softmax_scale, causal=causal, window_size=window_size)
 
 
-def flash_attn_func(q, k, v, dropout_p=0.0, softmax_scale=None, causal=False):
+def flash_attn_func(q, k, v, dropout_p=0.0, softmax_scale=None, causal=False, window_size=(-1, -1)):
     """Same as ``fwd`` (q, k, v in [B, H, N, d]); dropout must be 0."""
     if dropout_p != 0.0:
         raise NotImplementedError("dropout is not supported")
-    return fwd(q, k, v, softmax_scale=softmax_scale, causal=causal)
+    return fwd(q, k, v, softmax_scale=softmax_scale, causal=causal, window_size=window_size)

@@ -13,9 +13,9 @@
 namespace {
 
 typedef void (*fwd16_fn)(const uint16_t*, const uint16_t*, const uint16_t*, uint16_t*, float*, int, int,
-                         int, float);
+                         int, float, int, int);
 typedef void (*fwd32_fn)(const float*, const float*, const float*, float*, float*, int, int, int,
-                         float);
+                         float, int, int);
 
 template <class T>
 fwd16_fn pick16(int d, bool causal) {
@@ -72,7 +72,8 @@ extern "C" const char* fa_strerror(int status) {
     case FA_ERR_HEADDIM: return "head dimension must be 64, 128 or 256";
     case FA_ERR_DTYPE: return "dtype must be FA_F16, FA_BF16 or FA_F32";
     case FA_ERR_ALIGN: return "q, k, v, o must be 16-byte aligned and lse 4-byte aligned";
-    case FA_ERR_ARG: return "causal must be 0 or 1, scale finite, and o/lse must not overlap q/k/v";
+    case FA_ERR_ARG:
+      return "causal must be 0 or 1, scale finite, window sides >= -1, and o/lse must not overlap q/k/v";
     case FA_ERR_LAUNCH: return "the HIP runtime rejected the kernel launch";
   }
   return "unknown fa_status";
@@ -89,13 +90,15 @@ extern "C" int fa_fwd_grid(int B, int H, int N, int d, int causal, int dtype, lo
   return FA_OK;
 }
 
-extern "C" int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
-                      int N, int d, float scale, int causal, int dtype, void* stream) {
+extern "C" int fa_fwd_window(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                             int H, int N, int d, float scale, int causal, int window_left,
+                             int window_right, int dtype, void* stream) {
   long long nblocks = 0;
   int nqt = 0;
   int st = check_shape(B, H, N, d, causal, dtype, &nblocks, &nqt);
   if (st != FA_OK) return st;
   if (!std::isfinite(scale)) return FA_ERR_ARG;
+  if (window_left < -1 || window_right < -1) return FA_ERR_ARG;
   if (nblocks == 0) return FA_OK;  // B*H*N == 0: nothing to do
   if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
   if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o) & 15) return FA_ERR_ALIGN;
@@ -115,8 +118,14 @@ extern "C" int fa_fwd(const void* q, const void* k, const void* v, void* o, floa
   const float c = (float)((double)scale * 1.4426950408889634074);
   int n_arg = N, nqt_arg = nqt, nb_arg = (int)nblocks;
   float c_arg = c;
-  void* args[] = {(void*)&q, (void*)&k, (void*)&v, (void*)&o, (void*)&lse,
-                  (void*)&n_arg, (void*)&nqt_arg, (void*)&nb_arg, (void*)&c_arg};
+  // Visible keys of query i: i - wl .. i + wr, an unbounded side as 2^30
+  // (N is below 2^30, so no sum of a row index and a side overflows).
+  constexpr int kUnbounded = 1 << 30;
+  int wl = window_left < 0 ? kUnbounded : window_left;
+  int wr = window_right < 0 ? kUnbounded : window_right;
+  if (causal) wr = 0;
+  void* args[] = {(void*)&q, (void*)&k, (void*)&v, (void*)&o, (void*)&lse, (void*)&n_arg,
+                  (void*)&nqt_arg, (void*)&nb_arg, (void*)&c_arg, (void*)&wl, (void*)&wr};
 
   const void* fn = nullptr;
   if (dtype == FA_F32) {
@@ -130,4 +139,9 @@ extern "C" int fa_fwd(const void* q, const void* k, const void* v, void* o, floa
   const hipError_t e = hipLaunchKernel(fn, dim3((unsigned)nblocks), dim3(fa::kThreads), args, 0,
                                        (hipStream_t)stream);
   return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+extern "C" int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                      int N, int d, float scale, int causal, int dtype, void* stream) {
+  return fa_fwd_window(q, k, v, o, lse, B, H, N, d, scale, causal, -1, -1, dtype, stream);
 }

@@ -81,6 +81,9 @@ struct F16 {
   }
 };
 
+// Floor of a / b for b > 0 and any sign of a.
+__device__ __forceinline__ int floor_div(int a, int b) { return a >= 0 ? a / b : -((b - 1 - a) / b); }
+
 // Swap bits 2 and 3 of a key index inside its 16-key group (an involution).
 __device__ __forceinline__ int sigma(int m) {
   return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1);
@@ -116,31 +119,31 @@ __device__ __forceinline__ void decode_block(int nblocks, int nqt, bool causal, 
 
 // One online-softmax update for the 16 scores a lane holds: the 32x32 MFMA
 // tile s of keys kb + [0, 32) (register r: key kb + acc_row(r, hh)) for query
-// row qrow. Every row of the tile sees at least one key (the caller skips a
-// tile whose first key is past the rows or the sequence), so the new max is
-// finite. On return s holds P = exp2(S*c - m_new), unrounded fp32; returns
-// alpha = exp2(m_old - m_new).
-template <bool CAUSAL>
+// row qrow, which sees keys qrow - wl .. qrow + wr below N. On return s
+// holds P = exp2(S*c - m_new), unrounded fp32; returns alpha =
+// exp2(m_old - m_new).
 __device__ __forceinline__ float online_softmax(f32x16& s, float c, int kb, int qrow, int q0, int N,
-                                                int hh, float& m_run, float& l_run) {
-  const bool need_mask = (CAUSAL && kb + 31 > q0) || (kb + 32 > N);
+                                                int wl, int wr, int hh, float& m_run, float& l_run) {
+  const bool need_mask = kb + 31 > q0 + wr || kb + 32 > N || kb < q0 + 31 - wl;
   float mx = -INFINITY;
   if (need_mask || c < 0.f) {
-    // Scaled path: t = S * c for visible keys, -inf for masked ones.
+    // Scaled path: t = S * c for visible keys, -inf for masked ones. A row
+    // with no visible key so far keeps m = -inf (stand-in reference 0).
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int key = kb + acc_row(r, hh);
-      const bool ok = key < N && (!CAUSAL || key <= qrow);
+      const bool ok = key < N && key <= qrow + wr && key >= qrow - wl;
       s[r] = ok ? s[r] * c : -INFINITY;
       mx = fmaxf(mx, s[r]);
     }
     mx = wave_pair_max(mx);
     const float m_new = fmaxf(m_run, mx);
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    const float m_use = m_new == -INFINITY ? 0.f : m_new;
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
     float ls = 0.f;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      s[r] = __builtin_amdgcn_exp2f(s[r] - m_new);
+      s[r] = __builtin_amdgcn_exp2f(s[r] - m_use);
       ls += s[r];
     }
     l_run = alpha * l_run + ls;
@@ -299,7 +302,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
                           amdgpu_waves_per_eu(D >= 256 ? 1 : 2, D >= 256 ? 1 : 2)))
 void fwd16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                   const uint16_t* __restrict__ V, uint16_t* __restrict__ O,
-                  float* __restrict__ LSE, int N, int nqt, int nblocks, float c) {
+                  float* __restrict__ LSE, int N, int nqt, int nblocks, float c, int wl, int wr) {
   using G = Geo16<D>;
   typedef short s16x4 __attribute__((ext_vector_type(4)));
   typedef __attribute__((address_space(3))) s16x4* lds_s16x4_t;
@@ -339,8 +342,14 @@ void fwd16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K
     qf[s] ^= qflip;
   }
 
-  const int nkt = CAUSAL ? min((N + kBc - 1) / kBc, (qt * kBr + kBr - 1) / kBc + 1) : (N + kBc - 1) / kBc;
-  const int nfull = CAUSAL ? min(2 * qt, N / kBc) : N / kBc;  // leading tiles no row of the block masks
+  // Key tiles the block needs: t_lo .. t_lo + nkt - 1 (query i sees keys
+  // i - wl .. i + wr; wr is 0 when causal, and an unbounded side is 2^30).
+  // Tiles full_lo .. full_hi are visible to every row of the block.
+  const int q_lo = qt * kBr;
+  const int t_lo = max(q_lo - wl, 0) / kBc;
+  const int nkt = min(min(q_lo + kBr - 1, N - 1) + wr, N - 1) / kBc + 1 - t_lo;
+  const int full_lo = (max(q_lo + kBr - 1 - wl, 0) + kBc - 1) / kBc;
+  const int full_hi = floor_div(min(N, q_lo + wr + 1) - kBc, kBc);
 
   // Tile-invariant source offsets of this lane's copy slots.
   uint32_t koff[G::kKPW], voff[G::kVPW];
@@ -429,20 +438,21 @@ void fwd16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K
     }
   };
 
-  // Sets the scores of keys a row may not see (later than the row when
-  // causal, or past the end of the sequence) to -inf. Register r of sc0
+  // Sets the scores of keys a row may not see (outside qrow - wl ..
+  // qrow + wr, or past the end of the sequence) to -inf. Register r of sc0
   // holds key kbase + 8*hh + kc(r) with kc(r) = sigma(acc_row(r, 0)); sc1
-  // adds 32; a key is visible iff its kc <= lim.
+  // adds 32; a key is visible iff lo <= its kc <= lim.
   auto mask_tile = [&](int kbase) {
-    const int last = CAUSAL ? min(qrow, N - 1) : N - 1;
-    const int lim = last - kbase - 8 * hh;
+    const int lim = min(qrow + wr, N - 1) - kbase - 8 * hh;
+    const int lo = qrow - wl - kbase - 8 * hh;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int kc = 16 * (r >> 3) + 4 * ((r >> 2) & 1) + (r & 3);
-      sc0[r] = kc <= lim ? sc0[r] : -INFINITY;
-      sc1[r] = kc + 32 <= lim ? sc1[r] : -INFINITY;
+      sc0[r] = kc <= lim && kc >= lo ? sc0[r] : -INFINITY;
+      sc1[r] = kc + 32 <= lim && kc + 32 >= lo ? sc1[r] : -INFINITY;
     }
   };
+  auto is_full = [&](int t) { return t >= full_lo && t <= full_hi; };
 
   // P = exp2(S c - m) for the tile held in sc0/sc1, packed to the input
   // type (chunk cc of pf holds registers 8*(cc&1) .. +7 of sc0 for cc < 2,
@@ -480,15 +490,16 @@ void fwd16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K
     return mx == -INFINITY ? -INFINITY : mx * c;
   };
 
-  // Prologue: K0, K1 and V0 copied, then S_0.
-  issue_k(0, k0s);
-  if (nkt > 1) issue_k(1, k1s);
-  issue_v(0, v0s);
+  // Prologue: K0, K1 and V0 copied, then S_0 (tile indices below are
+  // relative to t_lo).
+  issue_k(t_lo, k0s);
+  if (nkt > 1) issue_k(t_lo + 1, k1s);
+  issue_v(t_lo, v0s);
   wait_vmcnt<0>();
   __syncthreads();
   s_tile(k0s, std::integral_constant<int, 0>{});
   __builtin_amdgcn_sched_barrier(0);
-  if (nfull == 0) mask_tile(0);
+  if (!is_full(t_lo)) mask_tile(t_lo * kBc);
 
   constexpr int kNK = G::kKPW, kNV = G::kVPW;  // copies per wave per tile
 
@@ -512,7 +523,7 @@ void fwd16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K
     __builtin_amdgcn_sched_barrier(0);
 
     // ---- block 1
-    issue_k(min(j + 2, nkt - 1), k_cur);
+    issue_k(t_lo + min(j + 2, nkt - 1), k_cur);
     if constexpr (PV) pv_tile(v_prev, pf_prev);
     float ls = exp_tile(m_run, pf_cur);
 #pragma unroll
@@ -532,12 +543,15 @@ void fwd16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K
     }
     __builtin_amdgcn_sched_barrier(0);
     // Some P of the tile may exceed 2^kTau (or m_run was still -inf): move
-    // the reference to the running max and redo P (rare).
+    // the reference to the running max and redo P (rare). A row that has
+    // seen no visible key yet (possible with a window) keeps m = -inf and
+    // gets P = 0 and l = 0 from a finite stand-in reference.
     if (__builtin_amdgcn_ballot_w64(!(ls <= kTauPow)) != 0) {
       const float m_new = fmaxf(m_run, tile_max());
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      const float m_use = m_new == -INFINITY ? 0.f : m_new;
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
       m_run = m_new;
-      ls = exp_tile(m_new, pf_cur);
+      ls = exp_tile(m_use, pf_cur);
       l_run *= alpha;
 #pragma unroll
       for (int t = 0; t < D / 32; ++t) acc[t] *= alpha;
@@ -552,10 +566,10 @@ void fwd16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K
       wait_vmcnt<kNK + kNV>();
       tile_barrier();
       __builtin_amdgcn_sched_barrier(0);
-      issue_v(j + 1, v_next);
+      issue_v(t_lo + j + 1, v_next);
       s_tile(k_next, std::integral_constant<int, kNV>{});
       __builtin_amdgcn_sched_barrier(0);
-      if (j + 1 >= nfull) mask_tile((j + 1) * kBc);
+      if (!is_full(t_lo + j + 1)) mask_tile((t_lo + j + 1) * kBc);
       // V_j landed before the next iteration reads it.
       wait_vmcnt<kNK + kNV>();
     } else {
@@ -607,7 +621,9 @@ void fwd16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K
 // +31 and the key half h = w >> 1 of every 64-key tile (keys 32h .. 32h+31):
 // the two waves of a row block run the online softmax over disjoint key
 // sets, and at the end the h = 1 wave hands its (m, l, O) to the h = 0 wave
-// through LDS, which merges them with the same rescaling rule.
+// through LDS, which merges them with the same rescaling rule. The window
+// (query i sees keys i - wl .. i + wr) only narrows the tile range and the
+// masks.
 // LDS: ks = K tile [64][D] floats with the 16-byte chunk swizzle ch ^ (m & 7)
 // (no key permutation); vs = V tile [64][D + 8] floats, rows padded by 32
 // bytes so the two lane halves (keys 4 apart) land on different banks.
@@ -618,7 +634,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
                           amdgpu_waves_per_eu(1, 1)))
 void fwd32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
                   const float* __restrict__ V, float* __restrict__ O,
-                  float* __restrict__ LSE, int N, int nqt, int nblocks, float c) {
+                  float* __restrict__ LSE, int N, int nqt, int nblocks, float c, int wl, int wr) {
   constexpr int DCH = D / 4;                  // 16-byte chunks per row
   constexpr int VSTRIDE = D + 8;              // floats per padded V row
   constexpr int KS_BYTES = kBc * D * 4;
@@ -658,8 +674,11 @@ void fwd32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
   for (int u = 0; u < D / 8; ++u)
     qf[u] = qrow < N ? *(const f32x4*)(Q + (size_t)qrow * D + 8 * u + 4 * hh) : f32x4{0, 0, 0, 0};
 
-  const int nkt_all = (N + kBc - 1) / kBc;
-  const int nkt = CAUSAL ? min(nkt_all, (qt * kBr32 + kBr32 - 1) / kBc + 1) : nkt_all;
+  // Key tiles the block needs (query i sees keys i - wl .. i + wr; wr is 0
+  // when causal, an unbounded side is 2^30).
+  const int q_lo = qt * kBr32;
+  const int t_lo = max(q_lo - wl, 0) / kBc;
+  const int t_end = min(min(q_lo + kBr32 - 1, N - 1) + wr, N - 1) / kBc + 1;
 
   f32x4 kreg[PF ? CH : 1], vreg[PF ? CH : 1];
 
@@ -702,19 +721,18 @@ void fwd32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
 #pragma unroll
   for (int t = 0; t < D / 32; ++t) acc[t] = f32x16{};
 
-  if constexpr (PF) gload(0);
-  for (int kt = 0; kt < nkt; ++kt) {
+  if constexpr (PF) gload(t_lo);
+  for (int kt = t_lo; kt < t_end; ++kt) {
     if constexpr (PF) swrite_regs();
     else copy_direct(kt);
     __syncthreads();
     if constexpr (PF) {
-      if (kt + 1 < nkt) gload(kt + 1);
+      if (kt + 1 < t_end) gload(kt + 1);
     }
-    // This wave's keys: kb .. kb + 31. A tile whose first key is past every
-    // row of the block (causal) or past the sequence is skipped; otherwise
-    // every row sees at least key kb (kb and q0 are multiples of 32).
+    // This wave's keys: kb .. kb + 31. A half tile no row of the wave can
+    // see is skipped.
     const int kb = kt * kBc + 32 * kh;
-    if ((!CAUSAL || kb <= q0 + 31) && kb < N) {
+    if (kb < N && kb <= q0 + 31 + wr && kb + 31 >= q0 - wl) {
       f32x16 s = {};
       const int krow = 32 * kh + n;
       const unsigned char* kr = ks + krow * (D * 4);
@@ -724,7 +742,7 @@ void fwd32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
 #pragma unroll
         for (int j = 0; j < 4; ++j) s = __builtin_amdgcn_mfma_f32_32x32x2f32(a[j], qf[u][j], s, 0, 0, 0);
       }
-      const float alpha = online_softmax<CAUSAL>(s, c, kb, qrow, q0, N, hh, m_run, l_run);
+      const float alpha = online_softmax(s, c, kb, qrow, q0, N, wl, wr, hh, m_run, l_run);
 #pragma unroll
       for (int t = 0; t < D / 32; ++t) acc[t] *= alpha;
 #pragma unroll
@@ -753,10 +771,12 @@ void fwd32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
   __syncthreads();
   if (kh == 1) return;
   {
+    // Either half may have seen no key of a row (then its m is -inf, l 0).
     const float m1 = xm[lane], l1 = xm[64 + lane];
-    const float m = fmaxf(m_run, m1);  // m_run is finite: this wave always sees key 0 of tile 0
-    const float a0 = __builtin_amdgcn_exp2f(m_run - m);
-    const float a1 = m1 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m1 - m);
+    const float m = fmaxf(m_run, m1);
+    const float m_use = m == -INFINITY ? 0.f : m;
+    const float a0 = __builtin_amdgcn_exp2f(m_run - m_use);
+    const float a1 = __builtin_amdgcn_exp2f(m1 - m_use);
 #pragma unroll
     for (int t = 0; t < D / 32; ++t)
 #pragma unroll
