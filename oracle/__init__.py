@@ -18,7 +18,8 @@ Sources (the web pages this work is built from):
   section 2 (softmax of the scaled product times V).
 * [P1] "Compiling Flash Attention 2.8.3 on Windows with an RTX 3090"
   (intelliparadigm.com): section 5.2 / 10.1 (``softmax_scale=None`` means
-  1/sqrt(d); ``causal`` flag; ``window_size`` local-attention window).
+  1/sqrt(d); ``causal`` flag; ``window_size`` local-attention window);
+  section 9.2 item 2 (the backward recomputes instead of storing).
 
 Parity status: every public function here is pinned by CPU tests (brute force
 in 40-digit decimal arithmetic, closed forms, invariants, a hand-derived
@@ -32,4 +33,5 @@ from .attention import (  # noqa: F401
     scores_ref,
     softmax_rows_ref,
 )
+from .backward import attention_bwd_ref  # noqa: F401
 from .bruteforce import attention_bruteforce  # noqa: F401
