@@ -122,6 +122,48 @@ def cpu_baseline(q, k, v, scale, causal, heads):
     }
 
 
+def bench_backward(fa, inputs, dev, stream, steps, warmup, no_parity):
+    import numpy as np
+    import torch
+
+    c = inputs.CONFIGS[SECONDARY]
+    log(f"[bench] backward on config {SECONDARY} ({c['name']}): inputs")
+    q, k, v = inputs.make_config(SECONDARY)
+    g = torch.Generator().manual_seed(43)
+    do = torch.randn(q.shape, generator=g, dtype=torch.float32).to(q.dtype)
+    qd, kd, vd, dod = (t.to(dev) for t in (q, k, v, do))
+    scale = 1.0 / math.sqrt(c["D"])
+    o, lse = fa.fwd(qd, kd, vd, softmax_scale=scale, causal=c["causal"])
+    dq, dk, dv = (torch.empty_like(qd) for _ in range(3))
+    delta = torch.empty(qd.shape[:3], dtype=torch.float32, device=dev)
+
+    def step():
+        fa.bwd(qd, kd, vd, o, lse, dod, softmax_scale=scale, causal=c["causal"], dq=dq, dk=dk, dv=dv,
+               delta=delta)
+
+    ok, err = None, float("nan")
+    if not no_parity:
+        from oracle import attention_bwd_ref
+
+        step()
+        torch.cuda.synchronize()
+        heads = slice(0, 2)
+        ref = attention_bwd_ref(*(t[:, heads].double().numpy() for t in (q, k, v, do)), scale, c["causal"])
+        errs = [float(np.abs(x[:, heads].double().cpu().numpy() - r).max() / max(np.abs(r).max(), 1.0))
+                for x, r in zip((dq, dk, dv), ref)]
+        err = max(errs)
+        ok = err <= 1e-2 and all(bool(torch.isfinite(x).all()) for x in (dq, dk, dv))
+        log(f"[bench] backward: max rel err dq/dk/dv = {errs} parity={'ok' if ok else 'FAIL'}")
+    _, per = time_launches(step, stream, steps, warmup)
+    kms = float(np.mean(per))
+    flops = 2.5 * metric_flops(c)
+    tf = flops / (kms * 1e-3) / 1e12
+    return {"workload": "gpt3-causal-d128 backward (dQ, dK, dV)", "B": c["B"], "H": c["H"], "N": c["N"],
+            "d": c["D"], "kernel_ms_mean": round(kms, 4), "tflops": round(tf, 2),
+            "frac": round(tf / PEAK_BF16_TFLOPS, 4), "flops_counted": "2.5x the forward's metric flops",
+            "parity_ok": ok, "max_rel_err_2_heads": err}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -247,6 +289,13 @@ def main():
                          "tflops": round(aw, 2), "frac": round(aw / PEAK_BF16_TFLOPS, 4),
                          "flops_counted": "4*d per visible (query, key) pair", "parity_ok": parw["ok"],
                          "max_abs_dO": parw["err_o"], "max_abs_dLSE": parw["err_l"]}
+    if not args.no_secondary:
+        # Backward pass on the GPT-3-shaped workload (fa_bwd: delta, dQ and
+        # dK/dV kernels), parity-checked on 2 of the 128 heads first.
+        # Flops: 2.5x the forward's (the five N x N x d products of the
+        # gradient, halved for causal), the usual accounting.
+        out["backward"] = bench_backward(fa, inputs, dev, stream, max(args.steps, 10), args.warmup,
+                                         args.no_parity)
     if args.calibrate_copy:
         log("[bench] copy calibration: 3 x 1 GiB device-to-device copy")
         src = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
@@ -259,7 +308,7 @@ def main():
         log(f"[bench] CPU baseline: fp64 oracle on {args.cpu_heads} head(s)")
         out["cpu_baseline"] = cpu_baseline(q, k, v, scale, True, args.cpu_heads)
     print(json.dumps(out), flush=True)
-    failed = [par["ok"]] + [out[k]["parity_ok"] for k in ("secondary", "fp32", "window") if k in out]
+    failed = [par["ok"]] + [out[k]["parity_ok"] for k in ("secondary", "fp32", "window", "backward") if k in out]
     if any(f is False for f in failed):
         sys.exit(1)
 

@@ -98,6 +98,44 @@ int fa_fwd_window(const void* q, const void* k, const void* v, void* o, float* l
                   int B, int H, int N, int d, float scale, int causal,
                   int window_left, int window_right, int dtype, void* stream);
 
+/*
+ * fa_bwd - enqueue the backward pass: the gradients dq, dk, dv of a loss
+ * whose gradient with respect to o is dout, for the forward pass fa_fwd_window
+ * computed with the same q, k, v, scale, causal and window.
+ *
+ * Operation (per batch b and head h; masked keys excluded as in the
+ * forward): P = exp(S - LSE) with S = scale q k^T, recomputed from q, k and
+ * the forward's lse rather than stored (the recomputation of section 9.2 of
+ * the flash-attn 2.8.3 build guide, intelliparadigm.com); then
+ *   dv = P^T dout,  dP = dout v^T,  delta_i = sum_c dout_ic o_ic,
+ *   dS = P * (dP - delta),  dq = scale dS k,  dk = scale dS^T q,
+ * the chain rule of the forward definition.
+ *
+ * q, k, v, o  device pointers, [B, H, N, d] contiguous, element type dtype:
+ *             the forward's inputs and output. Read only.
+ * lse         device pointer, [B, H, N] float32: the forward's lse. Read only.
+ * dout        device pointer, [B, H, N, d] contiguous, dtype: dLoss/do.
+ * dq, dk, dv  device pointers, [B, H, N, d] contiguous, dtype; written
+ *             (accumulated in float32, rounded to nearest even once).
+ * delta       device pointer, [B, H, N] float32; written with delta_i (it is
+ *             both a result and the scratch the kernels share).
+ * B, H, N, scale, causal, window_left, window_right, stream: as fa_fwd_window.
+ * d           64 or 128.
+ * dtype       FA_F16 or FA_BF16 (fp32 is not supported by the backward).
+ *
+ * Ownership, synchronisation and errors as fa_fwd: the caller owns every
+ * buffer, nothing is allocated, and three kernels are enqueued on stream in
+ * order (delta, then dq, then dk/dv); the result does not depend on
+ * scheduling (no atomics). The outputs dq, dk, dv, delta must not overlap
+ * each other or any input (FA_ERR_ARG). FA_ERR_HEADDIM for d other than 64
+ * or 128, FA_ERR_DTYPE for fp32 or an unknown dtype; all pointers 16-byte
+ * aligned except lse and delta (4-byte).
+ */
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+           const void* dout, void* dq, void* dk, void* dv, float* delta,
+           int B, int H, int N, int d, float scale, int causal,
+           int window_left, int window_right, int dtype, void* stream);
+
 /* Static text for a status code (never NULL). */
 const char* fa_strerror(int status);
 

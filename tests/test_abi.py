@@ -93,6 +93,34 @@ def test_python_window_argument_checked():
     assert fa._window((3, -1)) == (3, -1)
 
 
+BWD = dict(q=0x1000, k=0x2000, v=0x3000, o=0x4000, lse=0x5000, do=0x6000, dq=0x10000, dk=0x20000,
+           dv=0x30000, delta=0x40000, B=1, H=1, N=16, d=64, scale=0.125, causal=0, wl=-1, wr=-1, dtype=1)
+
+
+def call_bwd(**kw):
+    a = dict(BWD, **kw)
+    return fa.fa_bwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["do"], a["dq"], a["dk"], a["dv"], a["delta"],
+                     a["B"], a["H"], a["N"], a["d"], a["scale"], a["causal"], a["wl"], a["wr"], a["dtype"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(B=-1), -2), (dict(N=1 << 30), -2),
+    (dict(d=256), -3), (dict(d=32), -3),
+    (dict(dtype=2), -4), (dict(dtype=7), -4),
+    (dict(causal=3), -6), (dict(scale=float("nan")), -6), (dict(wl=-2), -6),
+    (dict(q=0), -1), (dict(do=0), -1), (dict(delta=0), -1), (dict(dv=0), -1),
+    (dict(dq=0x10008), -5), (dict(delta=0x40002), -5),
+    (dict(dq=0x1000), -6), (dict(dk=0x6000 + 32), -6), (dict(delta=0x5000), -6), (dict(dv=0x20000 + 64), -6),
+])
+def test_bwd_validation_errors(kw, code):
+    # every case fails a host-side check, so no HIP call is made
+    assert call_bwd(**kw) == code
+
+
+def test_bwd_zero_size_is_a_noop():
+    assert call_bwd(N=0, q=0, k=0, v=0, o=0, lse=0, do=0, dq=0, dk=0, dv=0, delta=0) == 0
+
+
 @pytest.mark.parametrize("kw", [dict(B=0), dict(H=0), dict(N=0)])
 def test_zero_size_is_a_noop(kw):
     # no launch and no pointer checks when there is nothing to compute

@@ -19,9 +19,16 @@ flash-attn 2.8.3 build guide, intelliparadigm.com, calls):
   causal=False) -> (o, lse)`` for a packed tensor [B, N, 3, H, d]; it splits
   and transposes the packed tensor into three [B, H, N, d] tensors (a copy)
   and calls ``fwd``; o and lse come back as [B, H, N, d] and [B, H, N].
-* ``fa_fwd(...)``, ``fa_fwd_window(...)``: the raw C entry points with the
-  same arguments as the C functions, for callers that manage their own
-  pointers and streams.
+* ``bwd(q, k, v, o, lse, do, softmax_scale=None, causal=False,
+  window_size=(-1, -1)) -> (dq, dk, dv)``: the backward pass (fp16/bf16,
+  d = 64 or 128), recomputing the attention weights from q, k and the
+  forward's lse (section 9.2 item 2 of the build guide).
+* ``attention(q, k, v, softmax_scale=None, causal=False,
+  window_size=(-1, -1)) -> o``: differentiable through torch autograd; its
+  backward calls ``bwd``.
+* ``fa_fwd(...)``, ``fa_fwd_window(...)``, ``fa_bwd(...)``: the raw C entry
+  points with the same arguments as the C functions, for callers that manage
+  their own pointers and streams.
 """
 
 from __future__ import annotations
@@ -44,7 +51,7 @@ STATUS = {
     -7: "FA_ERR_LAUNCH",
 }
 # Every symbol include/fa.h declares.
-EXPORTS = ("fa_fwd", "fa_fwd_window", "fa_strerror", "fa_fwd_grid")
+EXPORTS = ("fa_fwd", "fa_fwd_window", "fa_bwd", "fa_strerror", "fa_fwd_grid")
 
 _lib = None
 
@@ -77,6 +84,11 @@ def lib() -> ctypes.CDLL:
             ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_float,
             ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
         ]
+        h.fa_bwd.restype = ctypes.c_int
+        h.fa_bwd.argtypes = [ctypes.c_void_p] * 10 + [
+            ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_float,
+            ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+        ]
         h.fa_strerror.restype = ctypes.c_char_p
         h.fa_strerror.argtypes = [ctypes.c_int]
         h.fa_fwd_grid.restype = ctypes.c_int
@@ -102,6 +114,13 @@ def fa_fwd_window(q, k, v, o, lse, B, H, N, d, scale, causal, window_left, windo
     """Raw call of the windowed C entry point; pointers are ints (device addresses)."""
     return lib().fa_fwd_window(q, k, v, o, lse, B, H, N, d, scale, causal, window_left, window_right,
                                dtype, stream)
+
+
+def fa_bwd(q, k, v, o, lse, do, dq, dk, dv, delta, B, H, N, d, scale, causal, window_left,
+           window_right, dtype, stream=None) -> int:
+    """Raw call of the backward C entry point; pointers are ints (device addresses)."""
+    return lib().fa_bwd(q, k, v, o, lse, do, dq, dk, dv, delta, B, H, N, d, scale, causal, window_left,
+                        window_right, dtype, stream)
 
 
 def _window(window_size):
@@ -195,3 +214,90 @@ def flash_attn_func(q, k, v, dropout_p=0.0, softmax_scale=None, causal=False, wi
     if dropout_p != 0.0:
         raise NotImplementedError("dropout is not supported")
     return fwd(q, k, v, softmax_scale=softmax_scale, causal=causal, window_size=window_size)
+
+
+def bwd(q, k, v, o, lse, do, softmax_scale=None, causal=False, window_size=(-1, -1), dq=None, dk=None,
+        dv=None, delta=None):
+    """Backward pass on the GPU: returns (dq, dk, dv), each like q.
+
+    o and lse are the forward's outputs for the same q, k, v, scale, causal
+    and window; do is the gradient of the loss with respect to o. ``delta``
+    (optional, [B, H, N] float32) receives rowsum(do * o)."""
+    import torch
+
+    left, right = _window(window_size)
+    ts = (("q", q), ("k", k), ("v", v), ("o", o), ("do", do))
+    for name, t in ts:
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{name} must be a torch.Tensor")
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be on a GPU (no CPU path exists)")
+        if t.shape != q.shape or t.dim() != 4:
+            raise ValueError(f"{name} must be [B, H, N, d] like q, got {tuple(t.shape)}")
+        if t.dtype != q.dtype or t.device != q.device:
+            raise TypeError(f"{name} must match q's dtype and device")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    code = _dtype_code(q)
+    if code == FA_F32:
+        raise NotImplementedError("the backward pass supports float16 and bfloat16")
+    B, H, N, d = q.shape
+    if d not in (64, 128):
+        raise NotImplementedError(f"head dimension {d} is not supported by the backward pass (64, 128)")
+    if lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous() or lse.device != q.device:
+        raise ValueError("lse must be a contiguous float32 tensor [B, H, N] on q's device")
+    scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(q) if dk is None else dk
+    dv = torch.empty_like(q) if dv is None else dv
+    for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+        if t.shape != q.shape or t.dtype != q.dtype or not t.is_contiguous() or t.device != q.device:
+            raise ValueError(f"{name} must be a contiguous tensor like q")
+    if delta is None:
+        delta = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    if delta.shape != (B, H, N) or delta.dtype != torch.float32 or not delta.is_contiguous():
+        raise ValueError("delta must be a contiguous float32 tensor [B, H, N]")
+    with torch.cuda.device(q.device):
+        stream = torch.cuda.current_stream().cuda_stream
+        st = lib().fa_bwd(
+            q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), do.data_ptr(),
+            dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta.data_ptr(),
+            B, H, N, d, scale, int(bool(causal)), left, right, code, stream,
+        )
+    if st != 0:
+        raise FaError(st, strerror(st))
+    return dq, dk, dv
+
+
+_autograd_fn = None
+
+
+def _attention_function():
+    global _autograd_fn
+    if _autograd_fn is None:
+        import torch
+
+        class _Attention(torch.autograd.Function):
+            @staticmethod
+            def forward(ctx, q, k, v, softmax_scale, causal, window_size):
+                o, lse = fwd(q, k, v, softmax_scale=softmax_scale, causal=causal, window_size=window_size)
+                ctx.save_for_backward(q, k, v, o, lse)
+                ctx.args = (softmax_scale, causal, window_size)
+                return o
+
+            @staticmethod
+            def backward(ctx, do):
+                q, k, v, o, lse = ctx.saved_tensors
+                softmax_scale, causal, window_size = ctx.args
+                dq, dk, dv = bwd(q, k, v, o, lse, do.contiguous(), softmax_scale=softmax_scale, causal=causal,
+                                 window_size=window_size)
+                return dq, dk, dv, None, None, None
+
+        _autograd_fn = _Attention
+    return _autograd_fn
+
+
+def attention(q, k, v, softmax_scale=None, causal=False, window_size=(-1, -1)):
+    """Differentiable attention: o = softmax(scale q k^T [+ masks]) v, with
+    ``fwd`` forward and ``bwd`` backward under torch autograd."""
+    return _attention_function().apply(q, k, v, softmax_scale, causal, tuple(window_size))

@@ -1,0 +1,510 @@
+// fa_bwd.hip - backward pass of exact attention (fp16 / bf16 inputs, head
+// dimension 64 or 128): argument checks, kernels and launches of fa_bwd.
+//
+// The forward keeps only O and the row statistic LSE; the backward
+// recomputes the attention weights from Q, K and LSE instead of storing the
+// N x N matrix (the recomputation of section 9.2 of the flash-attn 2.8.3
+// build guide, intelliparadigm.com, and of section 7 of the RTX 4070
+// FlashAttention-2 page, jsqmd.com). The gradients are the chain rule of the
+// forward definition:
+//   P = exp(S - LSE) with S = scale Q K^T (masked keys excluded),
+//   dV = P^T dO,  dP = dO V^T,  D_i = sum_c dO_ic O_ic (= sum_j P_ij dP_ij),
+//   dS = P (dP - D),  dQ = scale dS K,  dK = scale dS^T Q.
+//
+// Three kernels on the caller's stream, no atomics (the result does not
+// depend on scheduling):
+//  * delta_kernel: D = rowsum(dO * O) into the caller's delta buffer;
+//  * dq_kernel: one workgroup per (batch*head, 128-row query tile), built
+//    like the forward: S^T = K Q^T and dP^T = V dO^T on the matrix cores
+//    with Q^T and dO^T held as B operands, P^T and dS^T per lane (each lane
+//    owns one query), then dQ^T += K^T dS^T with K^T read transposed from
+//    LDS and dS^T as the B operand;
+//  * dkdv_kernel: one workgroup per (batch*head, 128-key block), each wave
+//    owning 32 keys with K^T and V^T held as B operands; per 32-query step,
+//    S = Q K^T and dP = dO V^T with Q and dO from LDS, P and dS per lane
+//    (each lane owns one key), then dV^T += dO^T P and dK^T += Q^T dS with
+//    dO^T and Q^T read transposed from LDS.
+// The index tricks are the forward's: rows of an A operand are read through
+// the permutation sigma, which makes the accumulator of one product the B
+// operand layout of the next.
+//
+// LDS tiles hold rows of D 16-bit values with a row stride of max(2D, 256)
+// bytes; the 16-byte chunk c of row r is stored at chunk c ^ swz(r). With
+// swz(r) = ((r & 3) << 2) | ((r >> 2) & 3) both kinds of read are free of
+// bank conflicts: a 16-lane phase of 16-byte reads touches 16 rows whose
+// swz values are all different, and a 32-lane phase of transposed 8-byte
+// reads touches 4 consecutive rows x 64 bytes, which land in 4 different
+// 64-byte groups.
+#include <hip/hip_runtime.h>
+
+#include <climits>
+#include <cmath>
+#include <cstdint>
+#include <type_traits>
+
+#include "fa.h"
+#include "fa_kernels.h"
+
+namespace fa {
+namespace bwd {
+
+constexpr float kLog2e = 1.44269504088896340736f;
+
+template <int D>
+struct Tile {
+  static constexpr int kRS = 2 * D > 256 ? 2 * D : 256;  // LDS row stride, bytes
+  static constexpr int kCh = D / 8;                       // 16-byte chunks per row
+};
+
+__device__ __forceinline__ int swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+
+// Byte offset of 16-byte chunk c of row r in an LDS tile.
+template <int D>
+__device__ __forceinline__ int at(int r, int c) {
+  return r * Tile<D>::kRS + 16 * (c ^ swz(r));
+}
+
+template <class T>
+__device__ __forceinline__ float to_f32(uint32_t bits16) {
+  if constexpr (std::is_same<T, Bf16>::value) {
+    return __uint_as_float(bits16 << 16);
+  } else {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)bits16);
+  }
+}
+
+// Rows [0, R) of a row-major tile of D 16-bit values starting at src into
+// LDS; rows at or past nvalid are written as zeros.
+template <int D, int R>
+__device__ __forceinline__ void load_tile(const uint16_t* src, int nvalid, unsigned char* lds) {
+  constexpr int CH = D / 8;
+  static_assert((R * CH) % kThreads == 0, "whole chunks per thread");
+#pragma unroll
+  for (int k = 0; k < R * CH / kThreads; ++k) {
+    const int i = (int)threadIdx.x + k * kThreads;
+    const int r = i / CH, c = i - r * CH;
+    const u32x4 val = r < nvalid ? *(const u32x4*)(src + (size_t)r * D + 8 * c) : u32x4{0, 0, 0, 0};
+    *(u32x4*)(lds + at<D>(r, c)) = val;
+  }
+}
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4* lds_s16x4_t;
+
+// A operand of X^T B for the 16-row k-step ks and 32-column block tb of an
+// LDS tile X (rows are the k index): two transposed 8-byte reads, the lane
+// pattern of the forward kernel's V^T operand.
+template <int D>
+__device__ __forceinline__ u32x4 tr_operand(const unsigned char* tile, int ks, int tb, int lane) {
+  const int vb = lane >> 4, vj = lane & 15;
+  const int r0 = 16 * ks + 8 * (vb >> 1) + (vj >> 2);
+  const int c = 4 * tb + 2 * (vb & 1) + ((vj & 3) >> 1);
+  const int h8 = 8 * (vj & 1);
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t)as_lds(tile + at<D>(r0, c) + h8));
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t)as_lds(tile + at<D>(r0 + 4, c) + h8));
+  const u32x2 l2 = __builtin_bit_cast(u32x2, lo);
+  const u32x2 h2 = __builtin_bit_cast(u32x2, hi);
+  return u32x4{l2.x, l2.y, h2.x, h2.y};
+}
+
+// A operand of X B for k-step s (d = 16s .. 16s+15): MFMA row m is tile row
+// rbase + sigma(m), lane half hh reads chunk 2s + hh.
+template <int D>
+__device__ __forceinline__ u32x4 row_operand(const unsigned char* tile, int rbase, int s, int lane) {
+  return *(const u32x4*)(tile + at<D>(rbase + sigma(lane & 31), 2 * s + (lane >> 5)));
+}
+
+// Offset (0..31) of the row that register r of a 32x32 accumulator holds in
+// lane half hh, when the A operand's rows were read through sigma:
+// 8*hh + kc(r), the same map as the forward kernel's mask.
+__device__ __forceinline__ int perm_row(int r, int hh) {
+  return 8 * hh + 16 * (r >> 3) + 4 * ((r >> 2) & 1) + (r & 3);
+}
+
+// D_i = sum_c dO_ic O_ic, one row per D/8 consecutive lanes.
+template <class T, int D>
+__global__ __launch_bounds__(kThreads) void delta_kernel(const uint16_t* __restrict__ O,
+                                                         const uint16_t* __restrict__ dO,
+                                                         float* __restrict__ Dl, long long rows) {
+  constexpr int TPR = D / 8;
+  constexpr int RPB = kThreads / TPR;
+  const long long row = (long long)blockIdx.x * RPB + threadIdx.x / TPR;
+  const int c = threadIdx.x % TPR;
+  float acc = 0.f;
+  if (row < rows) {
+    const u32x4 a = *(const u32x4*)(O + row * D + 8 * c);
+    const u32x4 b = *(const u32x4*)(dO + row * D + 8 * c);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      acc += to_f32<T>(a[e] & 0xffffu) * to_f32<T>(b[e] & 0xffffu);
+      acc += to_f32<T>(a[e] >> 16) * to_f32<T>(b[e] >> 16);
+    }
+  }
+#pragma unroll
+  for (int o = TPR / 2; o > 0; o >>= 1) acc += __shfl_xor(acc, o, 64);
+  if (c == 0 && row < rows) Dl[row] = acc;
+}
+
+// dQ for one 128-row query tile. Query i sees keys i - wl .. i + wr (wr = 0
+// when causal; an unbounded side is 2^30).
+template <class T, int D, bool CAUSAL>
+__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(1, 1)))
+void dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+               const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
+               const float* __restrict__ LSE, const float* __restrict__ Dl, uint16_t* __restrict__ dQ,
+               int N, int nqt, int nblocks, float c, float scale, int wl, int wr) {
+  __shared__ __attribute__((aligned(16))) unsigned char ks[kBc * Tile<D>::kRS];
+  __shared__ __attribute__((aligned(16))) unsigned char vs[kBc * Tile<D>::kRS];
+
+  int bh, qt;
+  decode_block(nblocks, nqt, CAUSAL, bh, qt);
+  const size_t base = (size_t)bh * (size_t)N * D;
+  Q += base;
+  K += base;
+  V += base;
+  dO += base;
+  dQ += base;
+  LSE += (size_t)bh * N;
+  Dl += (size_t)bh * N;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n = lane & 31;
+  const int hh = lane >> 5;
+  const int q0 = qt * kBr + 32 * wave;
+  const int qrow = q0 + n;
+
+  // Q^T and dO^T as B operands: lane (n, hh), k-step s holds row qrow,
+  // columns 16s + 8hh .. +7.
+  u32x4 qf[D / 16], gf[D / 16];
+#pragma unroll
+  for (int s = 0; s < D / 16; ++s) {
+    qf[s] = qrow < N ? *(const u32x4*)(Q + (size_t)qrow * D + 16 * s + 8 * hh) : u32x4{0, 0, 0, 0};
+    gf[s] = qrow < N ? *(const u32x4*)(dO + (size_t)qrow * D + 16 * s + 8 * hh) : u32x4{0, 0, 0, 0};
+  }
+  // Rows past N get P = 0 (exp2(-inf)) and so contribute nothing.
+  const float lse2 = qrow < N ? LSE[qrow] * kLog2e : INFINITY;
+  const float dl = qrow < N ? Dl[qrow] : 0.f;
+
+  const int q_lo = qt * kBr;
+  const int t_lo = max(q_lo - wl, 0) / kBc;
+  const int t_end = min(min(q_lo + kBr - 1, N - 1) + wr, N - 1) / kBc + 1;
+
+  f32x16 acc[D / 32];
+#pragma unroll
+  for (int t = 0; t < D / 32; ++t) acc[t] = f32x16{};
+
+  for (int t = t_lo; t < t_end; ++t) {
+    __syncthreads();
+    load_tile<D, kBc>(K + (size_t)t * kBc * D, N - t * kBc, ks);
+    load_tile<D, kBc>(V + (size_t)t * kBc * D, N - t * kBc, vs);
+    __syncthreads();
+    const int kbase = t * kBc;
+    if (kbase > q0 + 31 + wr || kbase + kBc - 1 < q0 - wl) continue;  // no key visible to the wave
+
+    // S^T (keys x queries) and dP^T for keys 0..31 (x0) and 32..63 (x1).
+    f32x16 s0 = {}, s1 = {}, p0 = {}, p1 = {};
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) {
+      s0 = T::mfma(row_operand<D>(ks, 0, s, lane), qf[s], s0);
+      s1 = T::mfma(row_operand<D>(ks, 32, s, lane), qf[s], s1);
+      p0 = T::mfma(row_operand<D>(vs, 0, s, lane), gf[s], p0);
+      p1 = T::mfma(row_operand<D>(vs, 32, s, lane), gf[s], p1);
+    }
+    // P^T = exp2(S c - lse2) on visible keys, dS^T = P^T (dP^T - D), packed
+    // as the B operand of the next product: chunk cc holds keys
+    // 16cc + 8hh .. +7 of the tile.
+    const bool full = kbase + kBc - 1 <= q0 + wr && kbase >= q0 + 31 - wl && kbase + kBc <= N;
+    u32x4 dsp[4];
+#pragma unroll
+    for (int cc = 0; cc < 4; ++cc) {
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        float dsv[2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const int r = 8 * (cc & 1) + 2 * w + e;
+          const float sv = cc < 2 ? s0[r] : s1[r];
+          const float gv = cc < 2 ? p0[r] : p1[r];
+          const int key = kbase + 32 * (cc >> 1) + perm_row(r, hh);
+          const bool vis = full || (key < N && key <= qrow + wr && key >= qrow - wl);
+          const float p = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(sv, c, -lse2)) : 0.f;
+          dsv[e] = p * (gv - dl);
+        }
+        dsp[cc][w] = T::pack(dsv[0], dsv[1]);
+      }
+    }
+    // dQ^T += K^T dS^T.
+#pragma unroll
+    for (int cc = 0; cc < 4; ++cc)
+#pragma unroll
+      for (int tb = 0; tb < D / 32; ++tb) acc[tb] = T::mfma(tr_operand<D>(ks, cc, tb, lane), dsp[cc], acc[tb]);
+  }
+
+  if (qrow < N) {
+    uint16_t* row = dQ + (size_t)qrow * D;
+#pragma unroll
+    for (int tb = 0; tb < D / 32; ++tb) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        u32x2 out;
+        out.x = T::pack(acc[tb][4 * g] * scale, acc[tb][4 * g + 1] * scale);
+        out.y = T::pack(acc[tb][4 * g + 2] * scale, acc[tb][4 * g + 3] * scale);
+        *(u32x2*)(row + 32 * tb + 8 * g + 4 * hh) = out;
+      }
+    }
+  }
+}
+
+constexpr int kQT = 64;  // query rows per step of the dK/dV kernel
+
+// dK and dV for one 128-key block; wave w owns keys 32w .. 32w+31 of it.
+template <class T, int D, bool CAUSAL>
+__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(1, 1)))
+void dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+                 const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
+                 const float* __restrict__ LSE, const float* __restrict__ Dl, uint16_t* __restrict__ dK,
+                 uint16_t* __restrict__ dV, int N, int nkb, int nblocks, float c, float scale, int wl,
+                 int wr) {
+  __shared__ __attribute__((aligned(16))) unsigned char qs[kQT * Tile<D>::kRS];
+  __shared__ __attribute__((aligned(16))) unsigned char gs[kQT * Tile<D>::kRS];
+  __shared__ __attribute__((aligned(16))) float ls[kQT];  // LSE * log2(e), +inf past N
+  __shared__ __attribute__((aligned(16))) float dls[kQT];
+
+  // Key blocks in order: with a causal mask the first blocks have the most
+  // query tiles, so they start first.
+  int bh, kb;
+  decode_block(nblocks, nkb, false, bh, kb);
+  const size_t base = (size_t)bh * (size_t)N * D;
+  Q += base;
+  K += base;
+  V += base;
+  dO += base;
+  dK += base;
+  dV += base;
+  LSE += (size_t)bh * N;
+  Dl += (size_t)bh * N;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n = lane & 31;
+  const int hh = lane >> 5;
+  const int key0 = kb * kBr + 32 * wave;
+  const int krow = key0 + n;
+
+  // K^T and V^T as B operands: lane (n, hh), k-step s holds row krow,
+  // columns 16s + 8hh .. +7.
+  u32x4 kf[D / 16], vf[D / 16];
+#pragma unroll
+  for (int s = 0; s < D / 16; ++s) {
+    kf[s] = krow < N ? *(const u32x4*)(K + (size_t)krow * D + 16 * s + 8 * hh) : u32x4{0, 0, 0, 0};
+    vf[s] = krow < N ? *(const u32x4*)(V + (size_t)krow * D + 16 * s + 8 * hh) : u32x4{0, 0, 0, 0};
+  }
+
+  // Queries that see a key of the block: i - wl <= j <= i + wr.
+  const int k_lo = kb * kBr;
+  const int q_first = max(k_lo - wr, 0);
+  const int q_last = min(min(k_lo + kBr - 1, N - 1) + wl, N - 1);
+
+  f32x16 dk[D / 32], dv[D / 32];
+#pragma unroll
+  for (int t = 0; t < D / 32; ++t) dk[t] = dv[t] = f32x16{};
+
+  for (int qt = q_first / kQT; qt <= q_last / kQT; ++qt) {
+    const int qbase = qt * kQT;
+    __syncthreads();
+    load_tile<D, kQT>(Q + (size_t)qbase * D, N - qbase, qs);
+    load_tile<D, kQT>(dO + (size_t)qbase * D, N - qbase, gs);
+    if (tid < kQT) {
+      const int q = qbase + tid;
+      ls[tid] = q < N ? LSE[q] * kLog2e : INFINITY;
+      dls[tid] = q < N ? Dl[q] : 0.f;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int qh = 0; qh < kQT / 32; ++qh) {
+      const int qb = qbase + 32 * qh;
+      if (key0 > qb + 31 + wr || key0 + 31 < qb - wl) continue;  // no query of the step sees the wave's keys
+
+      // S = Q K^T and dP = dO V^T (queries x keys): lane (n, hh), register r
+      // holds query qb + perm_row(r, hh) and key krow.
+      f32x16 sa = {}, ga = {};
+#pragma unroll
+      for (int s = 0; s < D / 16; ++s) {
+        sa = T::mfma(row_operand<D>(qs, 32 * qh, s, lane), kf[s], sa);
+        ga = T::mfma(row_operand<D>(gs, 32 * qh, s, lane), vf[s], ga);
+      }
+      // Row statistics of the lane's 16 queries: 4 runs of 4 consecutive.
+      float l2[16], dl[16];
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int o = 32 * qh + perm_row(4 * g, hh);
+        const f32x4 a = *(const f32x4*)(ls + o);
+        const f32x4 b = *(const f32x4*)(dls + o);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          l2[4 * g + i] = a[i];
+          dl[4 * g + i] = b[i];
+        }
+      }
+      const bool full = krow < N && key0 + 31 <= qb + wr && key0 >= qb + 31 - wl;
+      u32x4 pp[2], dsp[2];
+#pragma unroll
+      for (int cc = 0; cc < 2; ++cc) {
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          float pv[2], dsv[2];
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            const int r = 8 * cc + 2 * w + e;
+            const int q = qb + perm_row(r, hh);
+            const bool vis = full || (krow < N && krow <= q + wr && krow >= q - wl);
+            const float p = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(sa[r], c, -l2[r])) : 0.f;
+            pv[e] = p;
+            dsv[e] = p * (ga[r] - dl[r]);
+          }
+          pp[cc][w] = T::pack(pv[0], pv[1]);
+          dsp[cc][w] = T::pack(dsv[0], dsv[1]);
+        }
+      }
+      // dV^T += dO^T P and dK^T += Q^T dS over the step's two 16-query k-steps.
+#pragma unroll
+      for (int cc = 0; cc < 2; ++cc) {
+#pragma unroll
+        for (int tb = 0; tb < D / 32; ++tb) {
+          dv[tb] = T::mfma(tr_operand<D>(gs, 2 * qh + cc, tb, lane), pp[cc], dv[tb]);
+          dk[tb] = T::mfma(tr_operand<D>(qs, 2 * qh + cc, tb, lane), dsp[cc], dk[tb]);
+        }
+      }
+    }
+  }
+
+  if (krow < N) {
+    uint16_t* krow_k = dK + (size_t)krow * D;
+    uint16_t* krow_v = dV + (size_t)krow * D;
+#pragma unroll
+    for (int tb = 0; tb < D / 32; ++tb) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        u32x2 ok, ov;
+        ok.x = T::pack(dk[tb][4 * g] * scale, dk[tb][4 * g + 1] * scale);
+        ok.y = T::pack(dk[tb][4 * g + 2] * scale, dk[tb][4 * g + 3] * scale);
+        ov.x = T::pack(dv[tb][4 * g], dv[tb][4 * g + 1]);
+        ov.y = T::pack(dv[tb][4 * g + 2], dv[tb][4 * g + 3]);
+        *(u32x2*)(krow_k + 32 * tb + 8 * g + 4 * hh) = ok;
+        *(u32x2*)(krow_v + 32 * tb + 8 * g + 4 * hh) = ov;
+      }
+    }
+  }
+}
+
+}  // namespace bwd
+}  // namespace fa
+
+namespace {
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+  return x < y + nb && y < x + na;
+}
+
+template <class T>
+struct BwdKernels {
+  const void* delta;
+  const void* dq;
+  const void* dkdv;
+  int rows_per_delta_block;
+};
+
+template <class T, int D>
+BwdKernels<T> pick_d(bool causal) {
+  return {(const void*)fa::bwd::delta_kernel<T, D>,
+          causal ? (const void*)fa::bwd::dq_kernel<T, D, true> : (const void*)fa::bwd::dq_kernel<T, D, false>,
+          causal ? (const void*)fa::bwd::dkdv_kernel<T, D, true> : (const void*)fa::bwd::dkdv_kernel<T, D, false>,
+          fa::kThreads / (D / 8)};
+}
+
+template <class T>
+BwdKernels<T> pick(int d, bool causal) {
+  return d == 64 ? pick_d<T, 64>(causal) : pick_d<T, 128>(causal);
+}
+
+}  // namespace
+
+extern "C" int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                      const void* dout, void* dq, void* dk, void* dv, float* delta, int B, int H, int N,
+                      int d, float scale, int causal, int window_left, int window_right, int dtype,
+                      void* stream) {
+  if (B < 0 || H < 0 || N < 0 || d < 0) return FA_ERR_SHAPE;
+  if (dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_DTYPE;
+  if (d != 64 && d != 128) return FA_ERR_HEADDIM;
+  if (causal != 0 && causal != 1) return FA_ERR_ARG;
+  if (!std::isfinite(scale)) return FA_ERR_ARG;
+  if (window_left < -1 || window_right < -1) return FA_ERR_ARG;
+  if (N > (1 << 30) - fa::kBr) return FA_ERR_SHAPE;
+  const long long tiles = (N + fa::kBr - 1) / fa::kBr;
+  const long long blocks = (long long)B * (long long)H * tiles;
+  if (blocks > INT_MAX) return FA_ERR_SHAPE;
+  if (blocks == 0) return FA_OK;
+  const void* ins[6] = {q, k, v, o, lse, dout};
+  void* outs[4] = {dq, dk, dv, delta};
+  for (const void* p : ins)
+    if (!p) return FA_ERR_NULL;
+  for (const void* p : outs)
+    if (!p) return FA_ERR_NULL;
+  if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o | (uintptr_t)dout | (uintptr_t)dq |
+       (uintptr_t)dk | (uintptr_t)dv) & 15)
+    return FA_ERR_ALIGN;
+  if (((uintptr_t)lse | (uintptr_t)delta) & 3) return FA_ERR_ALIGN;
+
+  const size_t rows = (size_t)B * H * N;
+  const size_t tb = rows * d * 2, rb = rows * sizeof(float);
+  const size_t in_bytes[6] = {tb, tb, tb, tb, rb, tb};
+  const size_t out_bytes[4] = {tb, tb, tb, rb};
+  for (int i = 0; i < 4; ++i) {
+    for (int j = 0; j < 6; ++j)
+      if (overlaps(outs[i], out_bytes[i], ins[j], in_bytes[j])) return FA_ERR_ARG;
+    for (int j = i + 1; j < 4; ++j)
+      if (overlaps(outs[i], out_bytes[i], outs[j], out_bytes[j])) return FA_ERR_ARG;
+  }
+
+  const void* kd;
+  const void* kq;
+  const void* kkv;
+  int rpb;
+  if (dtype == FA_BF16) {
+    const auto kk = pick<fa::Bf16>(d, causal != 0);
+    kd = kk.delta, kq = kk.dq, kkv = kk.dkdv, rpb = kk.rows_per_delta_block;
+  } else {
+    const auto kk = pick<fa::F16>(d, causal != 0);
+    kd = kk.delta, kq = kk.dq, kkv = kk.dkdv, rpb = kk.rows_per_delta_block;
+  }
+  hipStream_t st = (hipStream_t)stream;
+
+  long long nrows = (long long)rows;
+  void* dargs[] = {(void*)&o, (void*)&dout, (void*)&delta, (void*)&nrows};
+  const long long dblocks = ((long long)rows + rpb - 1) / rpb;
+  if (dblocks > INT_MAX) return FA_ERR_SHAPE;
+  if (hipLaunchKernel(kd, dim3((unsigned)dblocks), dim3(fa::kThreads), dargs, 0, st) != hipSuccess)
+    return FA_ERR_LAUNCH;
+
+  constexpr int kUnbounded = 1 << 30;
+  int wl = window_left < 0 ? kUnbounded : window_left;
+  int wr = window_right < 0 ? kUnbounded : window_right;
+  if (causal) wr = 0;
+  float c = (float)((double)scale * 1.4426950408889634074);
+  float sc = scale;
+  int n_arg = N, nt = (int)tiles, nb = (int)blocks;
+  const float* delta_c = delta;
+  void* qargs[] = {(void*)&q, (void*)&k, (void*)&v, (void*)&dout, (void*)&lse, (void*)&delta_c, (void*)&dq,
+                   (void*)&n_arg, (void*)&nt, (void*)&nb, (void*)&c, (void*)&sc, (void*)&wl, (void*)&wr};
+  if (hipLaunchKernel(kq, dim3((unsigned)blocks), dim3(fa::kThreads), qargs, 0, st) != hipSuccess)
+    return FA_ERR_LAUNCH;
+  void* kargs[] = {(void*)&q, (void*)&k, (void*)&v, (void*)&dout, (void*)&lse, (void*)&delta_c, (void*)&dk,
+                   (void*)&dv, (void*)&n_arg, (void*)&nt, (void*)&nb, (void*)&c, (void*)&sc, (void*)&wl,
+                   (void*)&wr};
+  if (hipLaunchKernel(kkv, dim3((unsigned)blocks), dim3(fa::kThreads), kargs, 0, st) != hipSuccess)
+    return FA_ERR_LAUNCH;
+  return FA_OK;
+}
