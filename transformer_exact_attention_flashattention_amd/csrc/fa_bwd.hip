@@ -73,20 +73,34 @@ __device__ __forceinline__ float to_f32(uint32_t bits16) {
   }
 }
 
-// Rows [0, R) of a row-major tile of D 16-bit values starting at src into
-// LDS; rows at or past nvalid are written as zeros.
+// A tile of R rows of D 16-bit values goes global -> registers -> LDS in
+// two steps, so that the global loads of the next tile can be in flight
+// while the current one is used: each thread moves CPT 16-byte chunks.
 template <int D, int R>
-__device__ __forceinline__ void load_tile(const uint16_t* src, int nvalid, unsigned char* lds) {
-  constexpr int CH = D / 8;
-  static_assert((R * CH) % kThreads == 0, "whole chunks per thread");
+struct TileRegs {
+  static constexpr int kCh = D / 8;
+  static constexpr int kCPT = R * kCh / kThreads;
+  static_assert((R * kCh) % kThreads == 0, "whole chunks per thread");
+  u32x4 v[kCPT];
+
+  // Rows [0, R) starting at src; rows at or past nvalid read as zeros.
+  __device__ __forceinline__ void load(const uint16_t* src, int nvalid) {
 #pragma unroll
-  for (int k = 0; k < R * CH / kThreads; ++k) {
-    const int i = (int)threadIdx.x + k * kThreads;
-    const int r = i / CH, c = i - r * CH;
-    const u32x4 val = r < nvalid ? *(const u32x4*)(src + (size_t)r * D + 8 * c) : u32x4{0, 0, 0, 0};
-    *(u32x4*)(lds + at<D>(r, c)) = val;
+    for (int k = 0; k < kCPT; ++k) {
+      const int i = (int)threadIdx.x + k * kThreads;
+      const int r = i / kCh, c = i - r * kCh;
+      v[k] = r < nvalid ? *(const u32x4*)(src + (size_t)r * D + 8 * c) : u32x4{0, 0, 0, 0};
+    }
   }
-}
+  __device__ __forceinline__ void store(unsigned char* lds) const {
+#pragma unroll
+    for (int k = 0; k < kCPT; ++k) {
+      const int i = (int)threadIdx.x + k * kThreads;
+      const int r = i / kCh, c = i - r * kCh;
+      *(u32x4*)(lds + at<D>(r, c)) = v[k];
+    }
+  }
+};
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4* lds_s16x4_t;
@@ -147,8 +161,9 @@ __global__ __launch_bounds__(kThreads) void delta_kernel(const uint16_t* __restr
 
 // dQ for one 128-row query tile. Query i sees keys i - wl .. i + wr (wr = 0
 // when causal; an unbounded side is 2^30).
+// Two waves per SIMD (two workgroups per compute unit), within 256 registers.
 template <class T, int D, bool CAUSAL>
-__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(1, 1)))
+__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(2, 2)))
 void dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
                const float* __restrict__ LSE, const float* __restrict__ Dl, uint16_t* __restrict__ dQ,
@@ -194,51 +209,64 @@ void dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
 #pragma unroll
   for (int t = 0; t < D / 32; ++t) acc[t] = f32x16{};
 
+  // Tiles go global -> registers -> LDS without a prefetch: at two
+  // workgroups per compute unit the other workgroup's work covers the load
+  // latency, and the registers a prefetch needs would not fit (measured:
+  // faster than prefetching at one workgroup per unit).
+  TileRegs<D, kBc> kr, vr;
   for (int t = t_lo; t < t_end; ++t) {
     __syncthreads();
-    load_tile<D, kBc>(K + (size_t)t * kBc * D, N - t * kBc, ks);
-    load_tile<D, kBc>(V + (size_t)t * kBc * D, N - t * kBc, vs);
+    kr.load(K + (size_t)t * kBc * D, N - t * kBc);
+    vr.load(V + (size_t)t * kBc * D, N - t * kBc);
+    kr.store(ks);
+    vr.store(vs);
     __syncthreads();
     const int kbase = t * kBc;
     if (kbase > q0 + 31 + wr || kbase + kBc - 1 < q0 - wl) continue;  // no key visible to the wave
 
-    // S^T (keys x queries) and dP^T for keys 0..31 (x0) and 32..63 (x1).
-    f32x16 s0 = {}, s1 = {}, p0 = {}, p1 = {};
-#pragma unroll
-    for (int s = 0; s < D / 16; ++s) {
-      s0 = T::mfma(row_operand<D>(ks, 0, s, lane), qf[s], s0);
-      s1 = T::mfma(row_operand<D>(ks, 32, s, lane), qf[s], s1);
-      p0 = T::mfma(row_operand<D>(vs, 0, s, lane), gf[s], p0);
-      p1 = T::mfma(row_operand<D>(vs, 32, s, lane), gf[s], p1);
-    }
-    // P^T = exp2(S c - lse2) on visible keys, dS^T = P^T (dP^T - D), packed
-    // as the B operand of the next product: chunk cc holds keys
-    // 16cc + 8hh .. +7 of the tile.
     const bool full = kbase + kBc - 1 <= q0 + wr && kbase >= q0 + 31 - wl && kbase + kBc <= N;
-    u32x4 dsp[4];
+    // The tile in two halves of 32 keys (fewer live registers).
 #pragma unroll
-    for (int cc = 0; cc < 4; ++cc) {
+    for (int kh = 0; kh < 2; ++kh) {
+      // S^T (keys x queries) and dP^T for keys 32kh .. 32kh+31.
+      f32x16 sa = {}, pa = {};
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        float dsv[2];
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          const int r = 8 * (cc & 1) + 2 * w + e;
-          const float sv = cc < 2 ? s0[r] : s1[r];
-          const float gv = cc < 2 ? p0[r] : p1[r];
-          const int key = kbase + 32 * (cc >> 1) + perm_row(r, hh);
-          const bool vis = full || (key < N && key <= qrow + wr && key >= qrow - wl);
-          const float p = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(sv, c, -lse2)) : 0.f;
-          dsv[e] = p * (gv - dl);
-        }
-        dsp[cc][w] = T::pack(dsv[0], dsv[1]);
+      for (int s = 0; s < D / 16; ++s) {
+        sa = T::mfma(row_operand<D>(ks, 32 * kh, s, lane), qf[s], sa);
+        pa = T::mfma(row_operand<D>(vs, 32 * kh, s, lane), gf[s], pa);
       }
+      // P^T = exp2(S c - lse2) on visible keys (0 elsewhere), dS^T =
+      // P^T (dP^T - D), packed as the B operand of the next product: chunk cc
+      // holds keys 32kh + 16cc + 8hh .. +7 of the tile.
+      u32x4 dsp[2];
+      auto make_ds = [&](auto masked) {
+#pragma unroll
+        for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            float dsv[2];
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+              const int r = 8 * cc + 2 * w + e;
+              float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sa[r], c, -lse2));
+              if constexpr (decltype(masked)::value) {
+                const int key = kbase + 32 * kh + perm_row(r, hh);
+                p = key < N && key <= qrow + wr && key >= qrow - wl ? p : 0.f;
+              }
+              dsv[e] = p * (pa[r] - dl);
+            }
+            dsp[cc][w] = T::pack(dsv[0], dsv[1]);
+          }
+      };
+      if (full) make_ds(std::false_type{});
+      else make_ds(std::true_type{});
+      // dQ^T += K^T dS^T over the half's two 16-key k-steps.
+#pragma unroll
+      for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+        for (int tb = 0; tb < D / 32; ++tb)
+          acc[tb] = T::mfma(tr_operand<D>(ks, 2 * kh + cc, tb, lane), dsp[cc], acc[tb]);
     }
-    // dQ^T += K^T dS^T.
-#pragma unroll
-    for (int cc = 0; cc < 4; ++cc)
-#pragma unroll
-      for (int tb = 0; tb < D / 32; ++tb) acc[tb] = T::mfma(tr_operand<D>(ks, cc, tb, lane), dsp[cc], acc[tb]);
   }
 
   if (qrow < N) {
@@ -259,6 +287,9 @@ void dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
 constexpr int kQT = 64;  // query rows per step of the dK/dV kernel
 
 // dK and dV for one 128-key block; wave w owns keys 32w .. 32w+31 of it.
+// One wave per SIMD: K^T, V^T and the dK^T, dV^T accumulators alone take
+// 192 registers per lane at d = 128, so the next query tile is prefetched
+// into registers instead.
 template <class T, int D, bool CAUSAL>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(1, 1)))
 void dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
@@ -311,22 +342,38 @@ void dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
 #pragma unroll
   for (int t = 0; t < D / 32; ++t) dk[t] = dv[t] = f32x16{};
 
-  for (int qt = q_first / kQT; qt <= q_last / kQT; ++qt) {
+  const int qt_lo = q_first / kQT, qt_hi = q_last / kQT;
+  TileRegs<D, kQT> qr, gr;
+  float lr = 0.f, dr = 0.f;  // this thread's LSE and delta entry (threads 0 .. kQT-1)
+  auto gload = [&](int qt) {
     const int qbase = qt * kQT;
-    __syncthreads();
-    load_tile<D, kQT>(Q + (size_t)qbase * D, N - qbase, qs);
-    load_tile<D, kQT>(dO + (size_t)qbase * D, N - qbase, gs);
+    qr.load(Q + (size_t)qbase * D, N - qbase);
+    gr.load(dO + (size_t)qbase * D, N - qbase);
     if (tid < kQT) {
       const int q = qbase + tid;
-      ls[tid] = q < N ? LSE[q] * kLog2e : INFINITY;
-      dls[tid] = q < N ? Dl[q] : 0.f;
+      lr = q < N ? LSE[q] * kLog2e : INFINITY;
+      dr = q < N ? Dl[q] : 0.f;
+    }
+  };
+  gload(qt_lo);
+  for (int qt = qt_lo; qt <= qt_hi; ++qt) {
+    const int qbase = qt * kQT;
+    __syncthreads();
+    qr.store(qs);
+    gr.store(gs);
+    if (tid < kQT) {
+      ls[tid] = lr;
+      dls[tid] = dr;
     }
     __syncthreads();
+    if (qt < qt_hi) gload(qt + 1);  // next tile's loads overlap this tile's work
+    // Skip the step if no query of it sees a key of the wave; take the
+    // unmasked path if every query of it sees every key of the wave.
+    if (key0 > qbase + kQT - 1 + wr || key0 + 31 < qbase - wl) continue;
+    const bool full = key0 + 31 < N && key0 + 31 <= qbase + wr && key0 >= qbase + kQT - 1 - wl;
 #pragma unroll
     for (int qh = 0; qh < kQT / 32; ++qh) {
       const int qb = qbase + 32 * qh;
-      if (key0 > qb + 31 + wr || key0 + 31 < qb - wl) continue;  // no query of the step sees the wave's keys
-
       // S = Q K^T and dP = dO V^T (queries x keys): lane (n, hh), register r
       // holds query qb + perm_row(r, hh) and key krow.
       f32x16 sa = {}, ga = {};
@@ -348,7 +395,17 @@ void dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
           dl[4 * g + i] = b[i];
         }
       }
-      const bool full = krow < N && key0 + 31 <= qb + wr && key0 >= qb + 31 - wl;
+      // P = exp2(S c - lse2) on visible pairs (rows past N have lse2 = +inf
+      // and give 0), dS = P (dP - D); both packed as B operands: chunk cc
+      // holds queries qb + 16cc + 8hh .. +7.
+      if (!full) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int q = qb + perm_row(r, hh);
+          const bool vis = krow < N && krow <= q + wr && krow >= q - wl;
+          l2[r] = vis ? l2[r] : INFINITY;
+        }
+      }
       u32x4 pp[2], dsp[2];
 #pragma unroll
       for (int cc = 0; cc < 2; ++cc) {
@@ -358,9 +415,7 @@ void dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
 #pragma unroll
           for (int e = 0; e < 2; ++e) {
             const int r = 8 * cc + 2 * w + e;
-            const int q = qb + perm_row(r, hh);
-            const bool vis = full || (krow < N && krow <= q + wr && krow >= q - wl);
-            const float p = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(sa[r], c, -l2[r])) : 0.f;
+            const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sa[r], c, -l2[r]));
             pv[e] = p;
             dsv[e] = p * (ga[r] - dl[r]);
           }
