@@ -105,28 +105,47 @@ struct TileRegs {
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4* lds_s16x4_t;
 
-// A operand of X^T B for the 16-row k-step ks and 32-column block tb of an
-// LDS tile X (rows are the k index): two transposed 8-byte reads, the lane
-// pattern of the forward kernel's V^T operand.
+// A lane's LDS byte offsets for its operand reads, with the chunk swizzle
+// resolved once (swz depends on r & 15 only, so moving by 16 rows adds a
+// plain row offset that the reads take as an immediate).
 template <int D>
-__device__ __forceinline__ u32x4 tr_operand(const unsigned char* tile, int ks, int tb, int lane) {
-  const int vb = lane >> 4, vj = lane & 15;
-  const int r0 = 16 * ks + 8 * (vb >> 1) + (vj >> 2);
-  const int c = 4 * tb + 2 * (vb & 1) + ((vj & 3) >> 1);
-  const int h8 = 8 * (vj & 1);
-  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t)as_lds(tile + at<D>(r0, c) + h8));
-  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t)as_lds(tile + at<D>(r0 + 4, c) + h8));
-  const u32x2 l2 = __builtin_bit_cast(u32x2, lo);
-  const u32x2 h2 = __builtin_bit_cast(u32x2, hi);
-  return u32x4{l2.x, l2.y, h2.x, h2.y};
-}
+struct Operands {
+  int ro[D / 16];  // A operand of X B, k-step s: row sigma(n), chunk 2s + hh
+  int tl[D / 32];  // A operand of X^T B, 32-column block tb: low 8 bytes
+  int th[D / 32];  //   and high 8 bytes (rows 4 further), for 16-row step 0
 
-// A operand of X B for k-step s (d = 16s .. 16s+15): MFMA row m is tile row
-// rbase + sigma(m), lane half hh reads chunk 2s + hh.
-template <int D>
-__device__ __forceinline__ u32x4 row_operand(const unsigned char* tile, int rbase, int s, int lane) {
-  return *(const u32x4*)(tile + at<D>(rbase + sigma(lane & 31), 2 * s + (lane >> 5)));
-}
+  __device__ __forceinline__ explicit Operands(int lane) {
+    const int n = lane & 31, hh = lane >> 5;
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) ro[s] = at<D>(sigma(n), 2 * s + hh);
+    // Transposed reads (the lane pattern of the forward kernel's V^T
+    // operand): 16-lane block vb, lane vj reads rows r0 and r0 + 4, chunk
+    // 4tb + c0, half vj & 1.
+    const int vb = lane >> 4, vj = lane & 15;
+    const int r0 = 8 * (vb >> 1) + (vj >> 2);
+    const int c0 = 2 * (vb & 1) + ((vj & 3) >> 1);
+    const int h8 = 8 * (vj & 1);
+#pragma unroll
+    for (int tb = 0; tb < D / 32; ++tb) {
+      tl[tb] = at<D>(r0, 4 * tb + c0) + h8;
+      th[tb] = at<D>(r0 + 4, 4 * tb + c0) + h8;
+    }
+  }
+
+  // X B operand: rows rbase + sigma(m) (rbase a multiple of 16).
+  __device__ __forceinline__ u32x4 row(const unsigned char* tile, int rbase, int s) const {
+    return *(const u32x4*)(tile + rbase * Tile<D>::kRS + ro[s]);
+  }
+  // X^T B operand: 16-row k-step ks (rows 16ks ..), 32-column block tb.
+  __device__ __forceinline__ u32x4 tr(const unsigned char* tile, int ks, int tb) const {
+    const unsigned char* t = tile + 16 * ks * Tile<D>::kRS;
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t)as_lds(t + tl[tb]));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t)as_lds(t + th[tb]));
+    const u32x2 l2 = __builtin_bit_cast(u32x2, lo);
+    const u32x2 h2 = __builtin_bit_cast(u32x2, hi);
+    return u32x4{l2.x, l2.y, h2.x, h2.y};
+  }
+};
 
 // Offset (0..31) of the row that register r of a 32x32 accumulator holds in
 // lane half hh, when the A operand's rows were read through sigma:
@@ -188,6 +207,7 @@ void dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   const int hh = lane >> 5;
   const int q0 = qt * kBr + 32 * wave;
   const int qrow = q0 + n;
+  const Operands<D> op(lane);
 
   // Q^T and dO^T as B operands: lane (n, hh), k-step s holds row qrow,
   // columns 16s + 8hh .. +7.
@@ -232,8 +252,8 @@ void dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
       f32x16 sa = {}, pa = {};
 #pragma unroll
       for (int s = 0; s < D / 16; ++s) {
-        sa = T::mfma(row_operand<D>(ks, 32 * kh, s, lane), qf[s], sa);
-        pa = T::mfma(row_operand<D>(vs, 32 * kh, s, lane), gf[s], pa);
+        sa = T::mfma(op.row(ks, 32 * kh, s), qf[s], sa);
+        pa = T::mfma(op.row(vs, 32 * kh, s), gf[s], pa);
       }
       // P^T = exp2(S c - lse2) on visible keys (0 elsewhere), dS^T =
       // P^T (dP^T - D), packed as the B operand of the next product: chunk cc
@@ -265,7 +285,7 @@ void dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
       for (int cc = 0; cc < 2; ++cc)
 #pragma unroll
         for (int tb = 0; tb < D / 32; ++tb)
-          acc[tb] = T::mfma(tr_operand<D>(ks, 2 * kh + cc, tb, lane), dsp[cc], acc[tb]);
+          acc[tb] = T::mfma(op.tr(ks, 2 * kh + cc, tb), dsp[cc], acc[tb]);
     }
   }
 
@@ -323,6 +343,7 @@ void dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   const int hh = lane >> 5;
   const int key0 = kb * kBr + 32 * wave;
   const int krow = key0 + n;
+  const Operands<D> op(lane);
 
   // K^T and V^T as B operands: lane (n, hh), k-step s holds row krow,
   // columns 16s + 8hh .. +7.
@@ -375,13 +396,21 @@ void dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     for (int qh = 0; qh < kQT / 32; ++qh) {
       const int qb = qbase + 32 * qh;
       // S = Q K^T and dP = dO V^T (queries x keys): lane (n, hh), register r
-      // holds query qb + perm_row(r, hh) and key krow.
+      // holds query qb + perm_row(r, hh) and key krow. Reads run 8 ahead of
+      // the MFMAs.
       f32x16 sa = {}, ga = {};
 #pragma unroll
       for (int s = 0; s < D / 16; ++s) {
-        sa = T::mfma(row_operand<D>(qs, 32 * qh, s, lane), kf[s], sa);
-        ga = T::mfma(row_operand<D>(gs, 32 * qh, s, lane), vf[s], ga);
+        sa = T::mfma(op.row(qs, 32 * qh, s), kf[s], sa);
+        ga = T::mfma(op.row(gs, 32 * qh, s), vf[s], ga);
       }
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 8, 0);
+#pragma unroll
+      for (int i = 0; i < D / 8; ++i) {
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
       // Row statistics of the lane's 16 queries: 4 runs of 4 consecutive.
       float l2[16], dl[16];
 #pragma unroll
@@ -407,8 +436,7 @@ void dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
         }
       }
       u32x4 pp[2], dsp[2];
-#pragma unroll
-      for (int cc = 0; cc < 2; ++cc) {
+      auto make_chunk = [&](int cc) {
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
           float pv[2], dsv[2];
@@ -422,16 +450,38 @@ void dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
           pp[cc][w] = T::pack(pv[0], pv[1]);
           dsp[cc][w] = T::pack(dsv[0], dsv[1]);
         }
-      }
-      // dV^T += dO^T P and dK^T += Q^T dS over the step's two 16-query k-steps.
+      };
+      make_chunk(0);
+      __builtin_amdgcn_sched_barrier(0);
+      // dV^T += dO^T P and dK^T += Q^T dS over the step's two 16-query
+      // k-steps; the second chunk's exponentials run beside the first
+      // k-step's MFMAs.
 #pragma unroll
-      for (int cc = 0; cc < 2; ++cc) {
-#pragma unroll
-        for (int tb = 0; tb < D / 32; ++tb) {
-          dv[tb] = T::mfma(tr_operand<D>(gs, 2 * qh + cc, tb, lane), pp[cc], dv[tb]);
-          dk[tb] = T::mfma(tr_operand<D>(qs, 2 * qh + cc, tb, lane), dsp[cc], dk[tb]);
-        }
+      for (int tb = 0; tb < D / 32; ++tb) {
+        dv[tb] = T::mfma(op.tr(gs, 2 * qh, tb), pp[0], dv[tb]);
+        dk[tb] = T::mfma(op.tr(qs, 2 * qh, tb), dsp[0], dk[tb]);
       }
+      make_chunk(1);
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 8, 0);
+#pragma unroll
+      for (int i = 0; i < D / 16; ++i) {
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedValu, 6, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int tb = 0; tb < D / 32; ++tb) {
+        dv[tb] = T::mfma(op.tr(gs, 2 * qh + 1, tb), pp[1], dv[tb]);
+        dk[tb] = T::mfma(op.tr(qs, 2 * qh + 1, tb), dsp[1], dk[tb]);
+      }
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 8, 0);
+#pragma unroll
+      for (int i = 0; i < D / 16; ++i) {
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
 
