@@ -147,6 +147,52 @@ struct Operands {
   }
 };
 
+// Copies of a 64-row tile into an LDS tile of the swizzled layout by
+// buffer loads that write LDS directly (no registers): each wave
+// instruction fills 1 KiB, i.e. 4 LDS rows, 16 bytes per lane in lane
+// order; lane l of copy block b writes row 4b + l/16 at physical chunk l%16
+// and so fetches the logical chunk (l%16) ^ swz(row) of that row (for
+// d = 64 the second half of each 256-byte row is padding, filled with a
+// duplicate chunk). Wave w issues blocks w, w + 4, ...; they all share the
+// lane's row modulo 16, hence one source offset plus 16 rows per block.
+// Rows past the end of the sequence are outside the buffer's range.
+template <int D, int R>
+struct TileDma {
+  static constexpr int kBlocks = R * Tile<D>::kRS / 1024;
+  static constexpr int kPW = kBlocks / 4;  // copy instructions per wave
+  static_assert(kBlocks % 4 == 0, "blocks per wave");
+
+  __device__ static uint32_t lane_offset(int wave, int lane) {
+    const int row = 4 * wave + (lane >> 4);
+    int c = (lane & 15) ^ swz(row);
+    if (c >= D / 8) c &= D / 8 - 1;  // padding slot
+    return (uint32_t)(row * 2 * D + 16 * c);
+  }
+
+  __device__ static void issue(const uint16_t* src, int nvalid, unsigned char* lds, uint32_t off, int wave) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    const int rows = nvalid < R ? (nvalid > 0 ? nvalid : 0) : R;
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)src, (short)0, rows * 2 * D, kBufWord3);
+#pragma unroll
+    for (int i = 0; i < kPW; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, as_lds(lds + 1024 * (wave + 4 * i)), 16,
+                                               off + (uint32_t)(i * 16 * 2 * D), 0, 0, 0);
+#endif
+  }
+};
+
+// One row statistic per query of a 64-query step (LSE or delta) into LDS by
+// a 4-byte copy per lane; every wave copies the same 256 bytes, so that all
+// waves issue the same number of copies.
+__device__ __forceinline__ void dma_row_stat(const float* src, int nvalid, float* lds, int lane) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  const int rows = nvalid < 64 ? (nvalid > 0 ? nvalid : 0) : 64;
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)src, (short)0, rows * 4, kBufWord3);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, as_lds(lds), 4, (uint32_t)(4 * lane), 0, 0, 0);
+#endif
+}
+
 // Offset (0..31) of the row that register r of a 32x32 accumulator holds in
 // lane half hh, when the A operand's rows were read through sigma:
 // 8*hh + kc(r), the same map as the forward kernel's mask.
@@ -187,8 +233,11 @@ void dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
                const float* __restrict__ LSE, const float* __restrict__ Dl, uint16_t* __restrict__ dQ,
                int N, int nqt, int nblocks, float c, float scale, int wl, int wr) {
-  __shared__ __attribute__((aligned(16))) unsigned char ks[kBc * Tile<D>::kRS];
-  __shared__ __attribute__((aligned(16))) unsigned char vs[kBc * Tile<D>::kRS];
+  // Two LDS stages, each a K tile then a V tile, filled by direct copies
+  // one tile ahead.
+  constexpr int TB = kBc * Tile<D>::kRS;
+  __shared__ __attribute__((aligned(1024))) unsigned char st0[2 * TB];
+  __shared__ __attribute__((aligned(1024))) unsigned char st1[2 * TB];
 
   int bh, qt;
   decode_block(nblocks, nqt, CAUSAL, bh, qt);
@@ -229,20 +278,32 @@ void dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
 #pragma unroll
   for (int t = 0; t < D / 32; ++t) acc[t] = f32x16{};
 
-  // Tiles go global -> registers -> LDS without a prefetch: at two
-  // workgroups per compute unit the other workgroup's work covers the load
-  // latency, and the registers a prefetch needs would not fit (measured:
-  // faster than prefetching at one workgroup per unit).
-  TileRegs<D, kBc> kr, vr;
-  for (int t = t_lo; t < t_end; ++t) {
+  using Dma = TileDma<D, kBc>;
+  const uint32_t doff = Dma::lane_offset(wave, lane);
+  // Rows past N of a ragged last tile keep what the stage held; they are
+  // masked, and starting from zeros keeps them finite.
+  if (N % kBc != 0) {
+    for (int i = threadIdx.x; i < 2 * TB / 16; i += kThreads) {
+      ((u32x4*)st0)[i] = u32x4{0, 0, 0, 0};
+      ((u32x4*)st1)[i] = u32x4{0, 0, 0, 0};
+    }
     __syncthreads();
-    kr.load(K + (size_t)t * kBc * D, N - t * kBc);
-    vr.load(V + (size_t)t * kBc * D, N - t * kBc);
-    kr.store(ks);
-    vr.store(vs);
-    __syncthreads();
+  }
+  auto issue = [&](int t, unsigned char* st) {
+    Dma::issue(K + (size_t)t * kBc * D, N - t * kBc, st, doff, wave);
+    Dma::issue(V + (size_t)t * kBc * D, N - t * kBc, st + TB, doff, wave);
+  };
+
+  auto step = [&](int t, const unsigned char* st, unsigned char* st_next) {
+    const unsigned char* const ks = st;
+    const unsigned char* const vs = st + TB;
+    // Tile t landed (it is the only copy in flight), every wave's copies are
+    // visible and every wave is done with tile t - 1: refill its stage.
+    wait_vmcnt<0>();
+    tile_barrier();
+    if (t + 1 < t_end) issue(t + 1, st_next);
     const int kbase = t * kBc;
-    if (kbase > q0 + 31 + wr || kbase + kBc - 1 < q0 - wl) continue;  // no key visible to the wave
+    if (kbase > q0 + 31 + wr || kbase + kBc - 1 < q0 - wl) return;  // no key visible to the wave
 
     const bool full = kbase + kBc - 1 <= q0 + wr && kbase >= q0 + 31 - wl && kbase + kBc <= N;
     // The tile in two halves of 32 keys (fewer live registers).
@@ -287,7 +348,15 @@ void dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
         for (int tb = 0; tb < D / 32; ++tb)
           acc[tb] = T::mfma(op.tr(ks, 2 * kh + cc, tb), dsp[cc], acc[tb]);
     }
+  };
+
+  issue(t_lo, st0);
+  int t = t_lo;
+  for (; t + 1 < t_end; t += 2) {
+    step(t, st0, st1);
+    step(t + 1, st1, st0);
   }
+  if (t < t_end) step(t, st0, st1);
 
   if (qrow < N) {
     uint16_t* row = dQ + (size_t)qrow * D;
@@ -308,8 +377,9 @@ constexpr int kQT = 64;  // query rows per step of the dK/dV kernel
 
 // dK and dV for one 128-key block; wave w owns keys 32w .. 32w+31 of it.
 // One wave per SIMD: K^T, V^T and the dK^T, dV^T accumulators alone take
-// 192 registers per lane at d = 128, so the next query tile is prefetched
-// into registers instead.
+// 192 registers per lane at d = 128. Query tiles (Q, dO, LSE, delta) stream
+// through a ring of three LDS stages filled by direct copies issued two
+// steps ahead.
 template <class T, int D, bool CAUSAL>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(1, 1)))
 void dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
@@ -317,10 +387,14 @@ void dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                  const float* __restrict__ LSE, const float* __restrict__ Dl, uint16_t* __restrict__ dK,
                  uint16_t* __restrict__ dV, int N, int nkb, int nblocks, float c, float scale, int wl,
                  int wr) {
-  __shared__ __attribute__((aligned(16))) unsigned char qs[kQT * Tile<D>::kRS];
-  __shared__ __attribute__((aligned(16))) unsigned char gs[kQT * Tile<D>::kRS];
-  __shared__ __attribute__((aligned(16))) float ls[kQT];  // LSE * log2(e), +inf past N
-  __shared__ __attribute__((aligned(16))) float dls[kQT];
+  // One array per stage: Q tile, dO tile, LSE (natural log), delta. (Few
+  // distinct arrays, so that the compiler can still tell the copies into
+  // one stage from the reads of another and does not wait on them.)
+  constexpr int TB = kQT * Tile<D>::kRS;
+  constexpr int SB = 2 * TB + 2 * kQT * 4;
+  __shared__ __attribute__((aligned(1024))) unsigned char st0[SB];
+  __shared__ __attribute__((aligned(1024))) unsigned char st1[SB];
+  __shared__ __attribute__((aligned(1024))) unsigned char st2[SB];
 
   // Key blocks in order: with a causal mask the first blocks have the most
   // query tiles, so they start first.
@@ -344,6 +418,8 @@ void dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   const int key0 = kb * kBr + 32 * wave;
   const int krow = key0 + n;
   const Operands<D> op(lane);
+  using Dma = TileDma<D, kQT>;
+  const uint32_t doff = Dma::lane_offset(wave, lane);
 
   // K^T and V^T as B operands: lane (n, hh), k-step s holds row krow,
   // columns 16s + 8hh .. +7.
@@ -358,40 +434,50 @@ void dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   const int k_lo = kb * kBr;
   const int q_first = max(k_lo - wr, 0);
   const int q_last = min(min(k_lo + kBr - 1, N - 1) + wl, N - 1);
+  const int qt_lo = q_first / kQT, qt_hi = q_last / kQT;
+
+  // Rows past N of a ragged last tile keep whatever the stage held; they
+  // are masked, and starting from zeros keeps them finite.
+  if (N % kQT != 0) {
+    for (int i = tid; i < SB / 16; i += kThreads) {
+      ((u32x4*)st0)[i] = u32x4{0, 0, 0, 0};
+      ((u32x4*)st1)[i] = u32x4{0, 0, 0, 0};
+      ((u32x4*)st2)[i] = u32x4{0, 0, 0, 0};
+    }
+    __syncthreads();
+  }
 
   f32x16 dk[D / 32], dv[D / 32];
 #pragma unroll
   for (int t = 0; t < D / 32; ++t) dk[t] = dv[t] = f32x16{};
 
-  const int qt_lo = q_first / kQT, qt_hi = q_last / kQT;
-  TileRegs<D, kQT> qr, gr;
-  float lr = 0.f, dr = 0.f;  // this thread's LSE and delta entry (threads 0 .. kQT-1)
-  auto gload = [&](int qt) {
+  constexpr int kCopies = 2 * Dma::kPW + 2;  // per wave per step
+  auto issue = [&](int qt, unsigned char* st) {
     const int qbase = qt * kQT;
-    qr.load(Q + (size_t)qbase * D, N - qbase);
-    gr.load(dO + (size_t)qbase * D, N - qbase);
-    if (tid < kQT) {
-      const int q = qbase + tid;
-      lr = q < N ? LSE[q] * kLog2e : INFINITY;
-      dr = q < N ? Dl[q] : 0.f;
-    }
+    Dma::issue(Q + (size_t)qbase * D, N - qbase, st, doff, wave);
+    Dma::issue(dO + (size_t)qbase * D, N - qbase, st + TB, doff, wave);
+    dma_row_stat(LSE + qbase, N - qbase, (float*)(st + 2 * TB), lane);
+    dma_row_stat(Dl + qbase, N - qbase, (float*)(st + 2 * TB) + kQT, lane);
   };
-  gload(qt_lo);
-  for (int qt = qt_lo; qt <= qt_hi; ++qt) {
+
+  auto step = [&](int qt, const unsigned char* st, unsigned char* st_next) {
+    const unsigned char* const qs = st;
+    const unsigned char* const gs = st + TB;
+    const float* const ls = (const float*)(st + 2 * TB);
+    const float* const dls = ls + kQT;
+    // This step's copies landed (those of the next step may still fly),
+    // then every wave's copies are visible.
+    if (qt + 1 <= qt_hi) wait_vmcnt<kCopies>();
+    else wait_vmcnt<0>();
+    tile_barrier();
+    // The stage of step qt - 1 is free now: refill it with step qt + 2.
+    if (qt + 2 <= qt_hi) issue(qt + 2, st_next);
     const int qbase = qt * kQT;
-    __syncthreads();
-    qr.store(qs);
-    gr.store(gs);
-    if (tid < kQT) {
-      ls[tid] = lr;
-      dls[tid] = dr;
-    }
-    __syncthreads();
-    if (qt < qt_hi) gload(qt + 1);  // next tile's loads overlap this tile's work
     // Skip the step if no query of it sees a key of the wave; take the
     // unmasked path if every query of it sees every key of the wave.
-    if (key0 > qbase + kQT - 1 + wr || key0 + 31 < qbase - wl) continue;
-    const bool full = key0 + 31 < N && key0 + 31 <= qbase + wr && key0 >= qbase + kQT - 1 - wl;
+    if (key0 > qbase + kQT - 1 + wr || key0 + 31 < qbase - wl) return;
+    const bool full = key0 + 31 < N && qbase + kQT <= N && key0 + 31 <= qbase + wr &&
+                      key0 >= qbase + kQT - 1 - wl;
 #pragma unroll
     for (int qh = 0; qh < kQT / 32; ++qh) {
       const int qb = qbase + 32 * qh;
@@ -420,18 +506,18 @@ void dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
         const f32x4 b = *(const f32x4*)(dls + o);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          l2[4 * g + i] = a[i];
+          l2[4 * g + i] = a[i] * kLog2e;
           dl[4 * g + i] = b[i];
         }
       }
-      // P = exp2(S c - lse2) on visible pairs (rows past N have lse2 = +inf
-      // and give 0), dS = P (dP - D); both packed as B operands: chunk cc
-      // holds queries qb + 16cc + 8hh .. +7.
+      // P = exp2(S c - lse2) on visible pairs, dS = P (dP - D); both packed
+      // as B operands: chunk cc holds queries qb + 16cc + 8hh .. +7. An
+      // invisible pair (or a query past N) gets lse2 = +inf, hence P = 0.
       if (!full) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int q = qb + perm_row(r, hh);
-          const bool vis = krow < N && krow <= q + wr && krow >= q - wl;
+          const bool vis = krow < N && q < N && krow <= q + wr && krow >= q - wl;
           l2[r] = vis ? l2[r] : INFINITY;
         }
       }
@@ -483,7 +569,20 @@ void dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
       }
       __builtin_amdgcn_sched_barrier(0);
     }
+  };
+
+  // Prologue: the first two steps in flight; then three steps per turn of
+  // the ring (stage of step qt: (qt - qt_lo) % 3).
+  issue(qt_lo, st0);
+  if (qt_lo + 1 <= qt_hi) issue(qt_lo + 1, st1);
+  int qt = qt_lo;
+  for (; qt + 2 <= qt_hi; qt += 3) {
+    step(qt, st0, st2);
+    step(qt + 1, st1, st0);
+    step(qt + 2, st2, st1);
   }
+  if (qt <= qt_hi) step(qt, st0, st2);
+  if (qt + 1 <= qt_hi) step(qt + 1, st1, st0);
 
   if (krow < N) {
     uint16_t* krow_k = dK + (size_t)krow * D;
