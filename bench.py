@@ -164,6 +164,50 @@ def bench_backward(fa, inputs, dev, stream, steps, warmup, no_parity):
             "parity_ok": ok, "max_rel_err_2_heads": err}
 
 
+def bench_packed(fa, inputs, dev, stream, steps, warmup):
+    """The GPT-3-shaped workload stored as one packed [B, N, 3, H, d] tensor:
+    the kernel reads the q, k, v slices in place and writes o [B, N, H, d].
+    Timed beside the three copies that unpacking to [B, H, N, d] would cost
+    and the contiguous call on those copies; the strided result must be
+    bitwise equal to the contiguous one (whose parity the secondary entry
+    checks)."""
+    import numpy as np
+    import torch
+
+    c = inputs.CONFIGS[SECONDARY]
+    B, H, N, D = c["B"], c["H"], c["N"], c["D"]
+    log(f"[bench] packed layout of config {SECONDARY} ({c['name']}): inputs")
+    qkv = inputs.make_packed_qkv(B, N, H, D, c["dtype"]).to(dev)
+    sl = [qkv[:, :, i].transpose(1, 2) for i in range(3)]
+    o = torch.empty((B, N, H, D), dtype=qkv.dtype, device=dev)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    dst = [torch.empty((B, H, N, D), dtype=qkv.dtype, device=dev) for _ in range(3)]
+    oc, lsec = torch.empty_like(dst[0]), torch.empty_like(lse)
+
+    def strided():
+        fa.fwd(*sl, causal=c["causal"], out=o.transpose(1, 2), lse=lse)
+
+    def unpack():
+        for d_, s_ in zip(dst, sl):
+            d_.copy_(s_)
+
+    def contiguous():
+        fa.fwd(*dst, causal=c["causal"], out=oc, lse=lsec)
+
+    _, per_s = time_launches(strided, stream, steps, warmup)
+    _, per_u = time_launches(unpack, stream, steps, warmup)
+    _, per_c = time_launches(contiguous, stream, steps, warmup)
+    torch.cuda.synchronize()
+    same = bool(torch.equal(o.transpose(1, 2), oc)) and bool(torch.equal(lse, lsec))
+    log(f"[bench] packed: strided == contiguous bitwise: {same}")
+    ks, ku, kc = (float(np.mean(x)) for x in (per_s, per_u, per_c))
+    tf = metric_flops(c) / (ks * 1e-3) / 1e12
+    return {"workload": "gpt3-causal-d128, qkv packed [B, N, 3, H, d], o [B, N, H, d]", "kernel_ms_mean": round(ks, 4),
+            "tflops": round(tf, 2), "frac": round(tf / PEAK_BF16_TFLOPS, 4),
+            "contiguous_kernel_ms_mean": round(kc, 4), "unpack_copy_ms_mean": round(ku, 4),
+            "parity_ok": same, "parity": "bitwise equal to the contiguous call on unpacked copies"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -296,6 +340,7 @@ def main():
         # gradient, halved for causal), the usual accounting.
         out["backward"] = bench_backward(fa, inputs, dev, stream, max(args.steps, 10), args.warmup,
                                          args.no_parity)
+        out["packed"] = bench_packed(fa, inputs, dev, stream, max(args.steps, 20), args.warmup)
     if args.calibrate_copy:
         log("[bench] copy calibration: 3 x 1 GiB device-to-device copy")
         src = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
@@ -308,7 +353,8 @@ def main():
         log(f"[bench] CPU baseline: fp64 oracle on {args.cpu_heads} head(s)")
         out["cpu_baseline"] = cpu_baseline(q, k, v, scale, True, args.cpu_heads)
     print(json.dumps(out), flush=True)
-    failed = [par["ok"]] + [out[k]["parity_ok"] for k in ("secondary", "fp32", "window", "backward") if k in out]
+    failed = [par["ok"]] + [out[k]["parity_ok"] for k in ("secondary", "fp32", "window", "backward", "packed")
+                          if k in out]
     if any(f is False for f in failed):
         sys.exit(1)
 

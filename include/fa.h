@@ -41,8 +41,8 @@ typedef enum {
     FA_ERR_SHAPE = -2,   /* a size is negative or too large */
     FA_ERR_HEADDIM = -3, /* d is not 64, 128 or 256 */
     FA_ERR_DTYPE = -4,   /* dtype is not an fa_dtype */
-    FA_ERR_ALIGN = -5,   /* q, k, v, o not 16-byte aligned, or lse not 4-byte aligned */
-    FA_ERR_ARG = -6,     /* causal not 0/1, scale not finite, or outputs overlap inputs */
+    FA_ERR_ALIGN = -5,   /* a row of q, k, v, o not 16-byte aligned, or lse not 4-byte aligned */
+    FA_ERR_ARG = -6,     /* causal not 0/1, scale not finite, or an output overlaps */
     FA_ERR_LAUNCH = -7   /* the HIP runtime rejected the kernel launch */
 } fa_status;
 
@@ -99,6 +99,44 @@ int fa_fwd_window(const void* q, const void* k, const void* v, void* o, float* l
                   int window_left, int window_right, int dtype, void* stream);
 
 /*
+ * fa_fwd_strided - fa_fwd_window on strided views, so that the head slices
+ * of a packed tensor are read and written in place. The packed layouts are
+ * those of the user calls of sections 5.2 and 10.1 of the flash-attn 2.8.3
+ * build guide (intelliparadigm.com): qkv as [B, N, 3, H, d], and q, k, v or
+ * o as [B, N, H, d].
+ *
+ * strides  host pointer to 12 element strides, or NULL for contiguous
+ *          [B, H, N, d] operands: (batch, head, row) for q, then k, v and o,
+ *          i.e. element (b, h, i, c) of q is q[b*s[0] + h*s[1] + i*s[2] + c].
+ *          The head dimension itself is always contiguous. Read during the
+ *          call only. Examples (element strides): contiguous [B, H, N, d]:
+ *          (H*N*d, N*d, d); a [B, N, H, d] tensor: (N*H*d, d, H*d); slice t
+ *          of a packed [B, N, 3, H, d] tensor, whose base is qkv + t*H*d:
+ *          (3*N*H*d, d, 3*H*d).
+ *
+ * Requirements, checked on the host before any HIP call:
+ *  - strides >= 0 and row strides >= d (FA_ERR_SHAPE); a row stride of at
+ *    most 32 MiB in bytes (FA_ERR_SHAPE); the stride of a dimension of
+ *    extent 1 is ignored;
+ *  - every row start 16-byte aligned: base pointer and strides times the
+ *    element size multiples of 16 (FA_ERR_ALIGN);
+ *  - inputs may overlap one another (a head stride of 0 shares one K or V
+ *    among all heads); o must not overlap itself (each stride, taken in
+ *    increasing order over dimensions of extent > 1, at least the extent
+ *    of the smaller ones) nor share a byte with q, k or v, and lse (still a
+ *    contiguous [B, H, N] float32 array) must not overlap any of them
+ *    (FA_ERR_ARG). Two operands whose extents overlap are accepted as
+ *    disjoint when they have the same row stride P, batch strides that are
+ *    multiples of P, and disjoint byte sets modulo P (the slices of one
+ *    packed tensor); other overlapping extents are rejected.
+ *
+ * Everything else as fa_fwd_window, which is this call with strides = NULL.
+ */
+int fa_fwd_strided(const void* q, const void* k, const void* v, void* o, float* lse,
+                   const long long* strides, int B, int H, int N, int d, float scale,
+                   int causal, int window_left, int window_right, int dtype, void* stream);
+
+/*
  * fa_bwd - enqueue the backward pass: the gradients dq, dk, dv of a loss
  * whose gradient with respect to o is dout, for the forward pass fa_fwd_window
  * computed with the same q, k, v, scale, causal and window.
@@ -135,6 +173,41 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const flo
            const void* dout, void* dq, void* dk, void* dv, float* delta,
            int B, int H, int N, int d, float scale, int causal,
            int window_left, int window_right, int dtype, void* stream);
+
+/*
+ * fa_bwd_strided - fa_bwd on strided views (the layouts of fa_fwd_strided),
+ * so that the gradient of a packed [B, N, 3, H, d] qkv is written in place.
+ *
+ * strides  host pointer to 24 element strides, or NULL for contiguous
+ *          operands: (batch, head, row) for q, k, v, o, dout, dq, dk, dv in
+ *          this order. lse and delta stay contiguous [B, H, N] float32.
+ *
+ * The stride, alignment and extent rules of fa_fwd_strided apply to all
+ * eight operands. dq, dk and dv must each be free of self-overlap and share
+ * no byte with any other operand; delta must overlap nothing. The slices
+ * of one packed gradient tensor pass this test.
+ *
+ * Everything else as fa_bwd, which is this call with strides = NULL.
+ */
+int fa_bwd_strided(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                   const void* dout, void* dq, void* dk, void* dv, float* delta,
+                   const long long* strides, int B, int H, int N, int d, float scale,
+                   int causal, int window_left, int window_right, int dtype, void* stream);
+
+/*
+ * fa_fwd_strided_check, fa_bwd_strided_check - host-only validation: return
+ * the status that fa_fwd_strided / fa_bwd_strided (same arguments, without
+ * the stream) would return from their argument checks, without any HIP call
+ * or launch. The pointers are only compared, never dereferenced. A caller
+ * can use them to find out up front whether a layout is accepted.
+ */
+int fa_fwd_strided_check(const void* q, const void* k, const void* v, void* o, float* lse,
+                         const long long* strides, int B, int H, int N, int d, float scale,
+                         int causal, int window_left, int window_right, int dtype);
+int fa_bwd_strided_check(const void* q, const void* k, const void* v, const void* o,
+                         const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                         float* delta, const long long* strides, int B, int H, int N, int d,
+                         float scale, int causal, int window_left, int window_right, int dtype);
 
 /* Static text for a status code (never NULL). */
 const char* fa_strerror(int status);

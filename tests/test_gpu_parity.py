@@ -81,12 +81,16 @@ def test_config_full(cfg):
 
 
 def test_config2_packed_entry():
+    """The packed call reads the slices of qkv in place; o is [B, N, H, d]."""
     c = inputs.CONFIGS[2]
     qkv = inputs.make_packed_qkv(c["B"], c["N"], c["H"], c["D"], c["dtype"])
-    o, lse = fa.flash_attn_qkvpacked_func(qkv.cuda(), dropout_p=0.0, softmax_scale=None, causal=False)
+    qkvd = qkv.cuda()
+    o = fa.flash_attn_qkvpacked_func(qkvd, dropout_p=0.0, softmax_scale=None, causal=False)
+    assert o.shape == (c["B"], c["N"], c["H"], c["D"])
+    _, lse = fa.fwd(*(qkvd[:, :, i].transpose(1, 2) for i in range(3)))
     torch.cuda.synchronize()
     q, k, v = inputs.unpack_qkv(qkv)
-    check(o.cpu(), lse.cpu(), q, k, v, 1.0 / math.sqrt(c["D"]), False)
+    check(o.transpose(1, 2).cpu(), lse.cpu(), q, k, v, 1.0 / math.sqrt(c["D"]), False)
 
 
 def _sample_rows(N, seed):

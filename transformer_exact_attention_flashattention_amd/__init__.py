@@ -10,25 +10,36 @@ flash-attn 2.8.3 build guide, intelliparadigm.com, calls):
 
 * ``fwd(q, k, v, softmax_scale=None, causal=False, window_size=(-1, -1))
   -> (o, lse)`` with q, k, v of shape [B, H, N, d] (the layout of section 1.1
-  of "2.3 FlashAttention and IO-aware attention"), contiguous, on one GPU,
-  all of dtype float16, bfloat16 or float32; ``softmax_scale=None`` means
+  of "2.3 FlashAttention and IO-aware attention") on one GPU, all of dtype
+  float16, bfloat16 or float32. Any strides are accepted as long as the last
+  dimension is contiguous and rows are 16-byte aligned (a transposed view of
+  a [B, N, H, d] tensor is read in place); ``softmax_scale=None`` means
   1/sqrt(d); ``window_size=(left, right)`` restricts query i to keys
   i - left .. i + right (-1: unbounded side), the reading of the
   ``window_size`` argument that section 10.1 lists.
 * ``flash_attn_qkvpacked_func(qkv, dropout_p=0.0, softmax_scale=None,
-  causal=False) -> (o, lse)`` for a packed tensor [B, N, 3, H, d]; it splits
-  and transposes the packed tensor into three [B, H, N, d] tensors (a copy)
-  and calls ``fwd``; o and lse come back as [B, H, N, d] and [B, H, N].
+  causal=False, window_size=(-1, -1)) -> o`` for a packed tensor
+  [B, N, 3, H, d] (section 5.2): o is [B, N, H, d]. The q, k and v slices are
+  read in place (no copy), and the call is differentiable: its backward
+  writes the gradient of the packed tensor in place too.
+* ``flash_attn_func(q, k, v, dropout_p=0.0, softmax_scale=None,
+  causal=False, window_size=(-1, -1)) -> o`` for q, k, v of shape
+  [B, N, H, d] (the per-tensor form of the packed layout), o [B, N, H, d];
+  differentiable.
 * ``bwd(q, k, v, o, lse, do, softmax_scale=None, causal=False,
   window_size=(-1, -1)) -> (dq, dk, dv)``: the backward pass (fp16/bf16,
   d = 64 or 128), recomputing the attention weights from q, k and the
-  forward's lse (section 9.2 item 2 of the build guide).
+  forward's lse (section 9.2 item 2 of the build guide); strided views as
+  for ``fwd``, including the gradients passed in as dq, dk, dv.
 * ``attention(q, k, v, softmax_scale=None, causal=False,
-  window_size=(-1, -1)) -> o``: differentiable through torch autograd; its
-  backward calls ``bwd``.
-* ``fa_fwd(...)``, ``fa_fwd_window(...)``, ``fa_bwd(...)``: the raw C entry
-  points with the same arguments as the C functions, for callers that manage
-  their own pointers and streams.
+  window_size=(-1, -1)) -> o``: [B, H, N, d], differentiable through torch
+  autograd; its backward calls ``bwd``.
+* ``fa_fwd(...)``, ``fa_fwd_window(...)``, ``fa_fwd_strided(...)``,
+  ``fa_bwd(...)``, ``fa_bwd_strided(...)``: the raw C entry points with the
+  same arguments as the C functions (strides as a sequence of ints or None),
+  for callers that manage their own pointers and streams;
+  ``fa_fwd_strided_check(...)`` and ``fa_bwd_strided_check(...)`` run only
+  their host-side argument checks.
 """
 
 from __future__ import annotations
@@ -51,7 +62,8 @@ STATUS = {
     -7: "FA_ERR_LAUNCH",
 }
 # Every symbol include/fa.h declares.
-EXPORTS = ("fa_fwd", "fa_fwd_window", "fa_bwd", "fa_strerror", "fa_fwd_grid")
+EXPORTS = ("fa_fwd", "fa_fwd_window", "fa_fwd_strided", "fa_bwd", "fa_bwd_strided", "fa_strerror",
+           "fa_fwd_grid", "fa_fwd_strided_check", "fa_bwd_strided_check")
 
 _lib = None
 
@@ -84,11 +96,25 @@ def lib() -> ctypes.CDLL:
             ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_float,
             ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
         ]
+        h.fa_fwd_strided.restype = ctypes.c_int
+        h.fa_fwd_strided.argtypes = [ctypes.c_void_p] * 5 + [ctypes.POINTER(ctypes.c_longlong)] + [
+            ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_float,
+            ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+        ]
         h.fa_bwd.restype = ctypes.c_int
         h.fa_bwd.argtypes = [ctypes.c_void_p] * 10 + [
             ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_float,
             ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
         ]
+        h.fa_bwd_strided.restype = ctypes.c_int
+        h.fa_bwd_strided.argtypes = [ctypes.c_void_p] * 10 + [ctypes.POINTER(ctypes.c_longlong)] + [
+            ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_float,
+            ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+        ]
+        h.fa_fwd_strided_check.restype = ctypes.c_int
+        h.fa_fwd_strided_check.argtypes = h.fa_fwd_strided.argtypes[:-1]
+        h.fa_bwd_strided_check.restype = ctypes.c_int
+        h.fa_bwd_strided_check.argtypes = h.fa_bwd_strided.argtypes[:-1]
         h.fa_strerror.restype = ctypes.c_char_p
         h.fa_strerror.argtypes = [ctypes.c_int]
         h.fa_fwd_grid.restype = ctypes.c_int
@@ -116,11 +142,50 @@ def fa_fwd_window(q, k, v, o, lse, B, H, N, d, scale, causal, window_left, windo
                                dtype, stream)
 
 
+def _strides_arg(strides, n):
+    if strides is None:
+        return None
+    vals = [int(x) for x in strides]
+    if len(vals) != n:
+        raise ValueError(f"expected {n} strides, got {len(vals)}")
+    return (ctypes.c_longlong * n)(*vals)
+
+
+def fa_fwd_strided(q, k, v, o, lse, strides, B, H, N, d, scale, causal, window_left, window_right, dtype,
+                   stream=None) -> int:
+    """Raw call of the strided C entry point: strides holds 12 element
+    strides (batch, head, row of q, k, v, o) or is None (contiguous)."""
+    return lib().fa_fwd_strided(q, k, v, o, lse, _strides_arg(strides, 12), B, H, N, d, scale, causal,
+                                window_left, window_right, dtype, stream)
+
+
+def fa_fwd_strided_check(q, k, v, o, lse, strides, B, H, N, d, scale, causal, window_left, window_right,
+                         dtype) -> int:
+    """Status fa_fwd_strided would return from its checks; no HIP call."""
+    return lib().fa_fwd_strided_check(q, k, v, o, lse, _strides_arg(strides, 12), B, H, N, d, scale, causal,
+                                      window_left, window_right, dtype)
+
+
+def fa_bwd_strided_check(q, k, v, o, lse, do, dq, dk, dv, delta, strides, B, H, N, d, scale, causal,
+                         window_left, window_right, dtype) -> int:
+    """Status fa_bwd_strided would return from its checks; no HIP call."""
+    return lib().fa_bwd_strided_check(q, k, v, o, lse, do, dq, dk, dv, delta, _strides_arg(strides, 24), B, H,
+                                      N, d, scale, causal, window_left, window_right, dtype)
+
+
 def fa_bwd(q, k, v, o, lse, do, dq, dk, dv, delta, B, H, N, d, scale, causal, window_left,
            window_right, dtype, stream=None) -> int:
     """Raw call of the backward C entry point; pointers are ints (device addresses)."""
     return lib().fa_bwd(q, k, v, o, lse, do, dq, dk, dv, delta, B, H, N, d, scale, causal, window_left,
                         window_right, dtype, stream)
+
+
+def fa_bwd_strided(q, k, v, o, lse, do, dq, dk, dv, delta, strides, B, H, N, d, scale, causal, window_left,
+                   window_right, dtype, stream=None) -> int:
+    """Raw call of the strided backward entry point: strides holds 24 element
+    strides (batch, head, row of q, k, v, o, do, dq, dk, dv) or is None."""
+    return lib().fa_bwd_strided(q, k, v, o, lse, do, dq, dk, dv, delta, _strides_arg(strides, 24), B, H, N, d,
+                                scale, causal, window_left, window_right, dtype, stream)
 
 
 def _window(window_size):
@@ -152,43 +217,68 @@ def _dtype_code(t):
     return codes[t.dtype]
 
 
+def _check_view(name, t, shape, dtype, device):
+    """A [B, H, N, d] operand: a GPU tensor of the given shape, dtype and
+    device whose last dimension is contiguous; other strides are checked by
+    the library."""
+    import torch
+
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on a GPU (no CPU path exists)")
+    if t.dim() != 4:
+        raise ValueError(f"{name} must be [B, H, N, d], got shape {tuple(t.shape)}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must have dtype {dtype}, got {t.dtype}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} must be on {device}")
+    if t.shape[-1] > 1 and t.stride(-1) != 1:
+        raise ValueError(f"{name} must have a contiguous last dimension")
+
+
+def _check_rowstat(name, t, B, H, N, device):
+    import torch
+
+    if t.shape != (B, H, N) or t.dtype != torch.float32 or not t.is_contiguous() or t.device != device:
+        raise ValueError(f"{name} must be a contiguous float32 tensor [B, H, N] on q's device")
+
+
+def _strides(*ts):
+    out = []
+    for t in ts:
+        out.extend(t.stride()[:3])
+    return out
+
+
 def fwd(q, k, v, softmax_scale=None, causal=False, window_size=(-1, -1), out=None, lse=None):
-    """Attention forward on the GPU: returns (o [B,H,N,d], lse [B,H,N] fp32)."""
+    """Attention forward on the GPU: returns (o [B,H,N,d], lse [B,H,N] fp32).
+
+    q, k, v (and ``out`` if given) may be strided views; a new ``out`` is
+    contiguous."""
     import torch
 
     left, right = _window(window_size)
-    for name, t in (("q", q), ("k", k), ("v", v)):
-        if not isinstance(t, torch.Tensor):
-            raise TypeError(f"{name} must be a torch.Tensor")
-        if not t.is_cuda:
-            raise ValueError(f"{name} must be on a GPU (no CPU path exists)")
-        if t.dim() != 4:
-            raise ValueError(f"{name} must be [B, H, N, d], got shape {tuple(t.shape)}")
-        if not t.is_contiguous():
-            raise ValueError(f"{name} must be contiguous")
-    if not (q.shape == k.shape == v.shape):
-        raise ValueError(f"q, k, v shapes differ: {tuple(q.shape)} {tuple(k.shape)} {tuple(v.shape)}")
-    if not (q.dtype == k.dtype == v.dtype):
-        raise TypeError("q, k, v must share one dtype")
-    if not (q.device == k.device == v.device):
-        raise ValueError("q, k, v must be on one device")
+    _check_view("q", q, None, None, None)
     code = _dtype_code(q)
+    _check_view("k", k, q.shape, q.dtype, q.device)
+    _check_view("v", v, q.shape, q.dtype, q.device)
     B, H, N, d = q.shape
     if d not in (64, 128, 256):
         raise NotImplementedError(f"head dimension {d} is not supported (64, 128, 256)")
     scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
     if out is None:
-        out = torch.empty_like(q)
+        out = torch.empty((B, H, N, d), dtype=q.dtype, device=q.device)
     if lse is None:
         lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
-    if out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous() or out.device != q.device:
-        raise ValueError("out must be a contiguous tensor like q")
-    if lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous() or lse.device != q.device:
-        raise ValueError("lse must be a contiguous float32 tensor [B, H, N] on q's device")
+    _check_view("out", out, q.shape, q.dtype, q.device)
+    _check_rowstat("lse", lse, B, H, N, q.device)
     with torch.cuda.device(q.device):
         stream = torch.cuda.current_stream().cuda_stream
-        st = lib().fa_fwd_window(
-            q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+        st = fa_fwd_strided(
+            q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), _strides(q, k, v, out),
             B, H, N, d, scale, int(bool(causal)), left, right, code, stream,
         )
     if st != 0:
@@ -196,72 +286,43 @@ def fwd(q, k, v, softmax_scale=None, causal=False, window_size=(-1, -1), out=Non
     return out, lse
 
 
-def flash_attn_qkvpacked_func(qkv, dropout_p=0.0, softmax_scale=None, causal=False,
-                              window_size=(-1, -1), alibi_slopes=None, deterministic=False):
-    """Packed-QKV entry: qkv [B, N, 3, H, d] -> (o [B,H,N,d], lse [B,H,N])."""
-    if dropout_p != 0.0:
-        raise NotImplementedError("dropout is not supported")
-    if alibi_slopes is not None:
-        raise NotImplementedError("ALiBi is not supported")
-    if qkv.dim() != 5 or qkv.shape[2] != 3:
-        raise ValueError(f"qkv must be [B, N, 3, H, d], got {tuple(qkv.shape)}")
-    q, k, v = (qkv[:, :, i].permute(0, 2, 1, 3).contiguous() for i in range(3))
-    return fwd(q, k, v, softmax_scale=softmax_scale, causal=causal, window_size=window_size)
-
-
-def flash_attn_func(q, k, v, dropout_p=0.0, softmax_scale=None, causal=False, window_size=(-1, -1)):
-    """Same as ``fwd`` (q, k, v in [B, H, N, d]); dropout must be 0."""
-    if dropout_p != 0.0:
-        raise NotImplementedError("dropout is not supported")
-    return fwd(q, k, v, softmax_scale=softmax_scale, causal=causal, window_size=window_size)
-
-
 def bwd(q, k, v, o, lse, do, softmax_scale=None, causal=False, window_size=(-1, -1), dq=None, dk=None,
         dv=None, delta=None):
-    """Backward pass on the GPU: returns (dq, dk, dv), each like q.
+    """Backward pass on the GPU: returns (dq, dk, dv), each of q's shape.
 
     o and lse are the forward's outputs for the same q, k, v, scale, causal
-    and window; do is the gradient of the loss with respect to o. ``delta``
-    (optional, [B, H, N] float32) receives rowsum(do * o)."""
+    and window; do is the gradient of the loss with respect to o. Every
+    [B, H, N, d] operand may be a strided view (new gradients are
+    contiguous). ``delta`` (optional, [B, H, N] float32) receives
+    rowsum(do * o)."""
     import torch
 
     left, right = _window(window_size)
-    ts = (("q", q), ("k", k), ("v", v), ("o", o), ("do", do))
-    for name, t in ts:
-        if not isinstance(t, torch.Tensor):
-            raise TypeError(f"{name} must be a torch.Tensor")
-        if not t.is_cuda:
-            raise ValueError(f"{name} must be on a GPU (no CPU path exists)")
-        if t.shape != q.shape or t.dim() != 4:
-            raise ValueError(f"{name} must be [B, H, N, d] like q, got {tuple(t.shape)}")
-        if t.dtype != q.dtype or t.device != q.device:
-            raise TypeError(f"{name} must match q's dtype and device")
-        if not t.is_contiguous():
-            raise ValueError(f"{name} must be contiguous")
+    _check_view("q", q, None, None, None)
+    for name, t in (("k", k), ("v", v), ("o", o), ("do", do)):
+        _check_view(name, t, q.shape, q.dtype, q.device)
     code = _dtype_code(q)
     if code == FA_F32:
         raise NotImplementedError("the backward pass supports float16 and bfloat16")
     B, H, N, d = q.shape
     if d not in (64, 128):
         raise NotImplementedError(f"head dimension {d} is not supported by the backward pass (64, 128)")
-    if lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous() or lse.device != q.device:
-        raise ValueError("lse must be a contiguous float32 tensor [B, H, N] on q's device")
+    _check_rowstat("lse", lse, B, H, N, q.device)
     scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
-    dq = torch.empty_like(q) if dq is None else dq
-    dk = torch.empty_like(q) if dk is None else dk
-    dv = torch.empty_like(q) if dv is None else dv
+    new = lambda: torch.empty((B, H, N, d), dtype=q.dtype, device=q.device)  # noqa: E731
+    dq = new() if dq is None else dq
+    dk = new() if dk is None else dk
+    dv = new() if dv is None else dv
     for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
-        if t.shape != q.shape or t.dtype != q.dtype or not t.is_contiguous() or t.device != q.device:
-            raise ValueError(f"{name} must be a contiguous tensor like q")
+        _check_view(name, t, q.shape, q.dtype, q.device)
     if delta is None:
         delta = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
-    if delta.shape != (B, H, N) or delta.dtype != torch.float32 or not delta.is_contiguous():
-        raise ValueError("delta must be a contiguous float32 tensor [B, H, N]")
+    _check_rowstat("delta", delta, B, H, N, q.device)
     with torch.cuda.device(q.device):
         stream = torch.cuda.current_stream().cuda_stream
-        st = lib().fa_bwd(
+        st = fa_bwd_strided(
             q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), do.data_ptr(),
-            dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta.data_ptr(),
+            dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta.data_ptr(), _strides(q, k, v, o, do, dq, dk, dv),
             B, H, N, d, scale, int(bool(causal)), left, right, code, stream,
         )
     if st != 0:
@@ -269,35 +330,106 @@ def bwd(q, k, v, o, lse, do, softmax_scale=None, causal=False, window_size=(-1, 
     return dq, dk, dv
 
 
-_autograd_fn = None
+def _last_dim_contiguous(t):
+    return t if t.shape[-1] <= 1 or t.stride(-1) == 1 else t.contiguous()
 
 
-def _attention_function():
-    global _autograd_fn
-    if _autograd_fn is None:
+_autograd_fns = None
+
+
+def _autograd_functions():
+    """The torch.autograd.Function classes (built on first use, so that the
+    module imports without torch)."""
+    global _autograd_fns
+    if _autograd_fns is None:
         import torch
 
         class _Attention(torch.autograd.Function):
+            """q, k, v [B, H, N, d] (or [B, N, H, d] with bnhd=True) -> o of
+            the same layout."""
+
             @staticmethod
-            def forward(ctx, q, k, v, softmax_scale, causal, window_size):
-                o, lse = fwd(q, k, v, softmax_scale=softmax_scale, causal=causal, window_size=window_size)
+            def forward(ctx, q, k, v, softmax_scale, causal, window_size, bnhd):
+                t = (lambda x: x.transpose(1, 2)) if bnhd else (lambda x: x)
+                o = torch.empty(q.shape, dtype=q.dtype, device=q.device)
+                _, lse = fwd(t(q), t(k), t(v), softmax_scale=softmax_scale, causal=causal,
+                             window_size=window_size, out=t(o))
                 ctx.save_for_backward(q, k, v, o, lse)
-                ctx.args = (softmax_scale, causal, window_size)
+                ctx.args = (softmax_scale, causal, window_size, bnhd)
                 return o
 
             @staticmethod
             def backward(ctx, do):
                 q, k, v, o, lse = ctx.saved_tensors
-                softmax_scale, causal, window_size = ctx.args
-                dq, dk, dv = bwd(q, k, v, o, lse, do.contiguous(), softmax_scale=softmax_scale, causal=causal,
-                                 window_size=window_size)
-                return dq, dk, dv, None, None, None
+                softmax_scale, causal, window_size, bnhd = ctx.args
+                t = (lambda x: x.transpose(1, 2)) if bnhd else (lambda x: x)
+                grads = [torch.empty(q.shape, dtype=q.dtype, device=q.device) for _ in range(3)]
+                bwd(t(q), t(k), t(v), t(o), lse, t(_last_dim_contiguous(do)), softmax_scale=softmax_scale,
+                    causal=causal, window_size=window_size, dq=t(grads[0]), dk=t(grads[1]), dv=t(grads[2]))
+                return grads[0], grads[1], grads[2], None, None, None, None
 
-        _autograd_fn = _Attention
-    return _autograd_fn
+        class _AttentionQKVPacked(torch.autograd.Function):
+            """qkv [B, N, 3, H, d] -> o [B, N, H, d]; q, k, v and their
+            gradients are slices of the packed tensors, used in place."""
+
+            @staticmethod
+            def forward(ctx, qkv, softmax_scale, causal, window_size):
+                B, N, _, H, d = qkv.shape
+                o = torch.empty((B, N, H, d), dtype=qkv.dtype, device=qkv.device)
+                sl = [qkv[:, :, i].transpose(1, 2) for i in range(3)]
+                _, lse = fwd(*sl, softmax_scale=softmax_scale, causal=causal, window_size=window_size,
+                             out=o.transpose(1, 2))
+                ctx.save_for_backward(qkv, o, lse)
+                ctx.args = (softmax_scale, causal, window_size)
+                return o
+
+            @staticmethod
+            def backward(ctx, do):
+                qkv, o, lse = ctx.saved_tensors
+                softmax_scale, causal, window_size = ctx.args
+                dqkv = torch.empty(qkv.shape, dtype=qkv.dtype, device=qkv.device)
+                sl = [qkv[:, :, i].transpose(1, 2) for i in range(3)]
+                gl = [dqkv[:, :, i].transpose(1, 2) for i in range(3)]
+                bwd(*sl, o.transpose(1, 2), lse, _last_dim_contiguous(do).transpose(1, 2),
+                    softmax_scale=softmax_scale, causal=causal, window_size=window_size,
+                    dq=gl[0], dk=gl[1], dv=gl[2])
+                return dqkv, None, None, None
+
+        _autograd_fns = (_Attention, _AttentionQKVPacked)
+    return _autograd_fns
 
 
 def attention(q, k, v, softmax_scale=None, causal=False, window_size=(-1, -1)):
-    """Differentiable attention: o = softmax(scale q k^T [+ masks]) v, with
-    ``fwd`` forward and ``bwd`` backward under torch autograd."""
-    return _attention_function().apply(q, k, v, softmax_scale, causal, tuple(window_size))
+    """Differentiable attention: o = softmax(scale q k^T [+ masks]) v for
+    q, k, v [B, H, N, d], with ``fwd`` forward and ``bwd`` backward under
+    torch autograd."""
+    return _autograd_functions()[0].apply(q, k, v, softmax_scale, causal, tuple(_window(window_size)), False)
+
+
+def _no_dropout(dropout_p, alibi_slopes=None):
+    if dropout_p != 0.0:
+        raise NotImplementedError("dropout is not supported")
+    if alibi_slopes is not None:
+        raise NotImplementedError("ALiBi is not supported")
+
+
+def flash_attn_qkvpacked_func(qkv, dropout_p=0.0, softmax_scale=None, causal=False,
+                              window_size=(-1, -1), alibi_slopes=None, deterministic=False):
+    """Packed-QKV attention: qkv [B, N, 3, H, d] -> o [B, N, H, d],
+    differentiable. The slices of qkv are read in place; the backward is
+    deterministic whatever ``deterministic`` says (no atomics)."""
+    _no_dropout(dropout_p, alibi_slopes)
+    if qkv.dim() != 5 or qkv.shape[2] != 3:
+        raise ValueError(f"qkv must be [B, N, 3, H, d], got {tuple(qkv.shape)}")
+    return _autograd_functions()[1].apply(qkv, softmax_scale, causal, tuple(_window(window_size)))
+
+
+def flash_attn_func(q, k, v, dropout_p=0.0, softmax_scale=None, causal=False, window_size=(-1, -1),
+                    alibi_slopes=None, deterministic=False):
+    """Attention for q, k, v [B, N, H, d] -> o [B, N, H, d], differentiable;
+    inputs are read in place (any strides with a contiguous last dimension)."""
+    _no_dropout(dropout_p, alibi_slopes)
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if t.dim() != 4:
+            raise ValueError(f"{name} must be [B, N, H, d], got shape {tuple(t.shape)}")
+    return _autograd_functions()[0].apply(q, k, v, softmax_scale, causal, tuple(_window(window_size)), True)

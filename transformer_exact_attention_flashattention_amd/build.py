@@ -14,7 +14,8 @@ PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG_DIR)
 LIB_PATH = os.path.join(PKG_DIR, "libfa.so")
 SOURCES = [os.path.join(PKG_DIR, "csrc", "fa_fwd.hip"), os.path.join(PKG_DIR, "csrc", "fa_bwd.hip")]
-HEADERS = [os.path.join(ROOT, "include", "fa.h"), os.path.join(PKG_DIR, "csrc", "fa_kernels.h")]
+HEADERS = [os.path.join(ROOT, "include", "fa.h"), os.path.join(PKG_DIR, "csrc", "fa_kernels.h"),
+           os.path.join(PKG_DIR, "csrc", "fa_host.h")]
 
 # -packed-fp32-ops: keep hipcc from emitting packed fp32 VALU instructions.
 HIPCC_FLAGS = [

@@ -43,6 +43,7 @@
 #include <type_traits>
 
 #include "fa.h"
+#include "fa_host.h"
 #include "fa_kernels.h"
 
 namespace fa {
@@ -72,35 +73,6 @@ __device__ __forceinline__ float to_f32(uint32_t bits16) {
     return (float)__builtin_bit_cast(_Float16, (uint16_t)bits16);
   }
 }
-
-// A tile of R rows of D 16-bit values goes global -> registers -> LDS in
-// two steps, so that the global loads of the next tile can be in flight
-// while the current one is used: each thread moves CPT 16-byte chunks.
-template <int D, int R>
-struct TileRegs {
-  static constexpr int kCh = D / 8;
-  static constexpr int kCPT = R * kCh / kThreads;
-  static_assert((R * kCh) % kThreads == 0, "whole chunks per thread");
-  u32x4 v[kCPT];
-
-  // Rows [0, R) starting at src; rows at or past nvalid read as zeros.
-  __device__ __forceinline__ void load(const uint16_t* src, int nvalid) {
-#pragma unroll
-    for (int k = 0; k < kCPT; ++k) {
-      const int i = (int)threadIdx.x + k * kThreads;
-      const int r = i / kCh, c = i - r * kCh;
-      v[k] = r < nvalid ? *(const u32x4*)(src + (size_t)r * D + 8 * c) : u32x4{0, 0, 0, 0};
-    }
-  }
-  __device__ __forceinline__ void store(unsigned char* lds) const {
-#pragma unroll
-    for (int k = 0; k < kCPT; ++k) {
-      const int i = (int)threadIdx.x + k * kThreads;
-      const int r = i / kCh, c = i - r * kCh;
-      *(u32x4*)(lds + at<D>(r, c)) = v[k];
-    }
-  }
-};
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4* lds_s16x4_t;
@@ -155,29 +127,31 @@ struct Operands {
 // d = 64 the second half of each 256-byte row is padding, filled with a
 // duplicate chunk). Wave w issues blocks w, w + 4, ...; they all share the
 // lane's row modulo 16, hence one source offset plus 16 rows per block.
-// Rows past the end of the sequence are outside the buffer's range.
+// Global rows are rs >= 2D bytes apart (the row stride of the operand's
+// view); rows past the end of the sequence are outside the buffer's range.
 template <int D, int R>
 struct TileDma {
   static constexpr int kBlocks = R * Tile<D>::kRS / 1024;
   static constexpr int kPW = kBlocks / 4;  // copy instructions per wave
   static_assert(kBlocks % 4 == 0, "blocks per wave");
 
-  __device__ static uint32_t lane_offset(int wave, int lane) {
+  __device__ static uint32_t lane_offset(int wave, int lane, int rs) {
     const int row = 4 * wave + (lane >> 4);
     int c = (lane & 15) ^ swz(row);
     if (c >= D / 8) c &= D / 8 - 1;  // padding slot
-    return (uint32_t)(row * 2 * D + 16 * c);
+    return (uint32_t)row * (uint32_t)rs + (uint32_t)(16 * c);
   }
 
-  __device__ static void issue(const uint16_t* src, int nvalid, unsigned char* lds, uint32_t off, int wave) {
+  __device__ static void issue(const uint16_t* src, int nvalid, int rs, unsigned char* lds, uint32_t off,
+                               int wave) {
 #if defined(__HIP_DEVICE_COMPILE__)
     const int rows = nvalid < R ? (nvalid > 0 ? nvalid : 0) : R;
-    const __amdgpu_buffer_rsrc_t rs =
-        __builtin_amdgcn_make_buffer_rsrc((void*)src, (short)0, rows * 2 * D, kBufWord3);
+    const int range = rows > 0 ? (rows - 1) * rs + 2 * D : 0;
+    const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)src, (short)0, range, kBufWord3);
 #pragma unroll
     for (int i = 0; i < kPW; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, as_lds(lds + 1024 * (wave + 4 * i)), 16,
-                                               off + (uint32_t)(i * 16 * 2 * D), 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, as_lds(lds + 1024 * (wave + 4 * i)), 16,
+                                               off + (uint32_t)(i * 16) * (uint32_t)rs, 0, 0, 0);
 #endif
   }
 };
@@ -200,19 +174,22 @@ __device__ __forceinline__ int perm_row(int r, int hh) {
   return 8 * hh + 16 * (r >> 3) + 4 * ((r >> 2) & 1) + (r & 3);
 }
 
-// D_i = sum_c dO_ic O_ic, one row per D/8 consecutive lanes.
+// D_i = sum_c dO_ic O_ic, one row per D/8 consecutive lanes; rows are
+// numbered (b * H + h) * N + i, the layout of Dl.
 template <class T, int D>
 __global__ __launch_bounds__(kThreads) void delta_kernel(const uint16_t* __restrict__ O,
                                                          const uint16_t* __restrict__ dO,
-                                                         float* __restrict__ Dl, long long rows) {
+                                                         float* __restrict__ Dl, View vo, View vdo, int H,
+                                                         int N, long long rows) {
   constexpr int TPR = D / 8;
   constexpr int RPB = kThreads / TPR;
   const long long row = (long long)blockIdx.x * RPB + threadIdx.x / TPR;
   const int c = threadIdx.x % TPR;
   float acc = 0.f;
   if (row < rows) {
-    const u32x4 a = *(const u32x4*)(O + row * D + 8 * c);
-    const u32x4 b = *(const u32x4*)(dO + row * D + 8 * c);
+    const int bh = (int)(row / N), i = (int)(row - (long long)bh * N);
+    const u32x4 a = *(const u32x4*)(O + view_base(vo, bh, H) + (long long)i * vo.r + 8 * c);
+    const u32x4 b = *(const u32x4*)(dO + view_base(vdo, bh, H) + (long long)i * vdo.r + 8 * c);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       acc += to_f32<T>(a[e] & 0xffffu) * to_f32<T>(b[e] & 0xffffu);
@@ -232,7 +209,8 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgp
 void dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
                const float* __restrict__ LSE, const float* __restrict__ Dl, uint16_t* __restrict__ dQ,
-               int N, int nqt, int nblocks, float c, float scale, int wl, int wr) {
+               View vq, View vk, View vv, View vdo, View vdq, int H, int N, int nqt, int nblocks, float c,
+               float scale, int wl, int wr) {
   // Two LDS stages, each a K tile then a V tile, filled by direct copies
   // one tile ahead.
   constexpr int TB = kBc * Tile<D>::kRS;
@@ -241,14 +219,14 @@ void dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
 
   int bh, qt;
   decode_block(nblocks, nqt, CAUSAL, bh, qt);
-  const size_t base = (size_t)bh * (size_t)N * D;
-  Q += base;
-  K += base;
-  V += base;
-  dO += base;
-  dQ += base;
+  Q += view_base(vq, bh, H);
+  K += view_base(vk, bh, H);
+  V += view_base(vv, bh, H);
+  dO += view_base(vdo, bh, H);
+  dQ += view_base(vdq, bh, H);
   LSE += (size_t)bh * N;
   Dl += (size_t)bh * N;
+  const int ksb = 2 * vk.r, vsb = 2 * vv.r;  // K and V row strides, bytes
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -263,8 +241,8 @@ void dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   u32x4 qf[D / 16], gf[D / 16];
 #pragma unroll
   for (int s = 0; s < D / 16; ++s) {
-    qf[s] = qrow < N ? *(const u32x4*)(Q + (size_t)qrow * D + 16 * s + 8 * hh) : u32x4{0, 0, 0, 0};
-    gf[s] = qrow < N ? *(const u32x4*)(dO + (size_t)qrow * D + 16 * s + 8 * hh) : u32x4{0, 0, 0, 0};
+    qf[s] = qrow < N ? *(const u32x4*)(Q + (long long)qrow * vq.r + 16 * s + 8 * hh) : u32x4{0, 0, 0, 0};
+    gf[s] = qrow < N ? *(const u32x4*)(dO + (long long)qrow * vdo.r + 16 * s + 8 * hh) : u32x4{0, 0, 0, 0};
   }
   // Rows past N get P = 0 (exp2(-inf)) and so contribute nothing.
   const float lse2 = qrow < N ? LSE[qrow] * kLog2e : INFINITY;
@@ -279,7 +257,8 @@ void dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   for (int t = 0; t < D / 32; ++t) acc[t] = f32x16{};
 
   using Dma = TileDma<D, kBc>;
-  const uint32_t doff = Dma::lane_offset(wave, lane);
+  const uint32_t koff = Dma::lane_offset(wave, lane, ksb);
+  const uint32_t voff = Dma::lane_offset(wave, lane, vsb);
   // Rows past N of a ragged last tile keep what the stage held; they are
   // masked, and starting from zeros keeps them finite.
   if (N % kBc != 0) {
@@ -290,8 +269,8 @@ void dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     __syncthreads();
   }
   auto issue = [&](int t, unsigned char* st) {
-    Dma::issue(K + (size_t)t * kBc * D, N - t * kBc, st, doff, wave);
-    Dma::issue(V + (size_t)t * kBc * D, N - t * kBc, st + TB, doff, wave);
+    Dma::issue(K + (long long)(t * kBc) * vk.r, N - t * kBc, ksb, st, koff, wave);
+    Dma::issue(V + (long long)(t * kBc) * vv.r, N - t * kBc, vsb, st + TB, voff, wave);
   };
 
   auto step = [&](int t, const unsigned char* st, unsigned char* st_next) {
@@ -359,7 +338,7 @@ void dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   if (t < t_end) step(t, st0, st1);
 
   if (qrow < N) {
-    uint16_t* row = dQ + (size_t)qrow * D;
+    uint16_t* row = dQ + (long long)qrow * vdq.r;
 #pragma unroll
     for (int tb = 0; tb < D / 32; ++tb) {
 #pragma unroll
@@ -385,8 +364,8 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgp
 void dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                  const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
                  const float* __restrict__ LSE, const float* __restrict__ Dl, uint16_t* __restrict__ dK,
-                 uint16_t* __restrict__ dV, int N, int nkb, int nblocks, float c, float scale, int wl,
-                 int wr) {
+                 uint16_t* __restrict__ dV, View vq, View vk, View vv, View vdo, View vdk, View vdv, int H,
+                 int N, int nkb, int nblocks, float c, float scale, int wl, int wr) {
   // One array per stage: Q tile, dO tile, LSE (natural log), delta. (Few
   // distinct arrays, so that the compiler can still tell the copies into
   // one stage from the reads of another and does not wait on them.)
@@ -400,15 +379,15 @@ void dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   // query tiles, so they start first.
   int bh, kb;
   decode_block(nblocks, nkb, false, bh, kb);
-  const size_t base = (size_t)bh * (size_t)N * D;
-  Q += base;
-  K += base;
-  V += base;
-  dO += base;
-  dK += base;
-  dV += base;
+  Q += view_base(vq, bh, H);
+  K += view_base(vk, bh, H);
+  V += view_base(vv, bh, H);
+  dO += view_base(vdo, bh, H);
+  dK += view_base(vdk, bh, H);
+  dV += view_base(vdv, bh, H);
   LSE += (size_t)bh * N;
   Dl += (size_t)bh * N;
+  const int qsb = 2 * vq.r, gsb = 2 * vdo.r;  // Q and dO row strides, bytes
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -419,15 +398,16 @@ void dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   const int krow = key0 + n;
   const Operands<D> op(lane);
   using Dma = TileDma<D, kQT>;
-  const uint32_t doff = Dma::lane_offset(wave, lane);
+  const uint32_t qoff = Dma::lane_offset(wave, lane, qsb);
+  const uint32_t goff = Dma::lane_offset(wave, lane, gsb);
 
   // K^T and V^T as B operands: lane (n, hh), k-step s holds row krow,
   // columns 16s + 8hh .. +7.
   u32x4 kf[D / 16], vf[D / 16];
 #pragma unroll
   for (int s = 0; s < D / 16; ++s) {
-    kf[s] = krow < N ? *(const u32x4*)(K + (size_t)krow * D + 16 * s + 8 * hh) : u32x4{0, 0, 0, 0};
-    vf[s] = krow < N ? *(const u32x4*)(V + (size_t)krow * D + 16 * s + 8 * hh) : u32x4{0, 0, 0, 0};
+    kf[s] = krow < N ? *(const u32x4*)(K + (long long)krow * vk.r + 16 * s + 8 * hh) : u32x4{0, 0, 0, 0};
+    vf[s] = krow < N ? *(const u32x4*)(V + (long long)krow * vv.r + 16 * s + 8 * hh) : u32x4{0, 0, 0, 0};
   }
 
   // Queries that see a key of the block: i - wl <= j <= i + wr.
@@ -454,8 +434,8 @@ void dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   constexpr int kCopies = 2 * Dma::kPW + 2;  // per wave per step
   auto issue = [&](int qt, unsigned char* st) {
     const int qbase = qt * kQT;
-    Dma::issue(Q + (size_t)qbase * D, N - qbase, st, doff, wave);
-    Dma::issue(dO + (size_t)qbase * D, N - qbase, st + TB, doff, wave);
+    Dma::issue(Q + (long long)qbase * vq.r, N - qbase, qsb, st, qoff, wave);
+    Dma::issue(dO + (long long)qbase * vdo.r, N - qbase, gsb, st + TB, goff, wave);
     dma_row_stat(LSE + qbase, N - qbase, (float*)(st + 2 * TB), lane);
     dma_row_stat(Dl + qbase, N - qbase, (float*)(st + 2 * TB) + kQT, lane);
   };
@@ -585,8 +565,8 @@ void dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   if (qt + 1 <= qt_hi) step(qt + 1, st1, st0);
 
   if (krow < N) {
-    uint16_t* krow_k = dK + (size_t)krow * D;
-    uint16_t* krow_v = dV + (size_t)krow * D;
+    uint16_t* krow_k = dK + (long long)krow * vdk.r;
+    uint16_t* krow_v = dV + (long long)krow * vdv.r;
 #pragma unroll
     for (int tb = 0; tb < D / 32; ++tb) {
 #pragma unroll
@@ -607,11 +587,6 @@ void dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
 }  // namespace fa
 
 namespace {
-
-bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
-  const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
-  return x < y + nb && y < x + na;
-}
 
 template <class T>
 struct BwdKernels {
@@ -636,10 +611,18 @@ BwdKernels<T> pick(int d, bool causal) {
 
 }  // namespace
 
-extern "C" int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
-                      const void* dout, void* dq, void* dk, void* dv, float* delta, int B, int H, int N,
-                      int d, float scale, int causal, int window_left, int window_right, int dtype,
-                      void* stream) {
+namespace {
+
+// Everything fa_bwd_strided checks, without a HIP call. On FA_OK, blocks is
+// the launch size (0: nothing to do) and view the kernels' operands.
+struct BwdPlan {
+  long long tiles = 0, blocks = 0;
+  fa::View view[8];
+};
+
+int plan_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
+             void* dq, void* dk, void* dv, float* delta, const long long* strides, int B, int H, int N, int d,
+             float scale, int causal, int window_left, int window_right, int dtype, BwdPlan* plan) {
   if (B < 0 || H < 0 || N < 0 || d < 0) return FA_ERR_SHAPE;
   if (dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_DTYPE;
   if (d != 64 && d != 128) return FA_ERR_HEADDIM;
@@ -650,28 +633,59 @@ extern "C" int fa_bwd(const void* q, const void* k, const void* v, const void* o
   const long long tiles = (N + fa::kBr - 1) / fa::kBr;
   const long long blocks = (long long)B * (long long)H * tiles;
   if (blocks > INT_MAX) return FA_ERR_SHAPE;
+  if ((long long)B * H * N > (long long)INT_MAX * (fa::kThreads / 16)) return FA_ERR_SHAPE;  // delta grid
+  plan->tiles = tiles;
+  plan->blocks = blocks;
   if (blocks == 0) return FA_OK;
-  const void* ins[6] = {q, k, v, o, lse, dout};
-  void* outs[4] = {dq, dk, dv, delta};
-  for (const void* p : ins)
+  // The eight [B, H, N, d] operands in the order of the strides array: five
+  // inputs, then the three gradients.
+  const void* ptrs[8] = {q, k, v, o, dout, dq, dk, dv};
+  for (const void* p : ptrs)
     if (!p) return FA_ERR_NULL;
-  for (const void* p : outs)
-    if (!p) return FA_ERR_NULL;
-  if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o | (uintptr_t)dout | (uintptr_t)dq |
-       (uintptr_t)dk | (uintptr_t)dv) & 15)
-    return FA_ERR_ALIGN;
+  if (!lse || !delta) return FA_ERR_NULL;
   if (((uintptr_t)lse | (uintptr_t)delta) & 3) return FA_ERR_ALIGN;
-
-  const size_t rows = (size_t)B * H * N;
-  const size_t tb = rows * d * 2, rb = rows * sizeof(float);
-  const size_t in_bytes[6] = {tb, tb, tb, tb, rb, tb};
-  const size_t out_bytes[4] = {tb, tb, tb, rb};
-  for (int i = 0; i < 4; ++i) {
-    for (int j = 0; j < 6; ++j)
-      if (overlaps(outs[i], out_bytes[i], ins[j], in_bytes[j])) return FA_ERR_ARG;
-    for (int j = i + 1; j < 4; ++j)
-      if (overlaps(outs[i], out_bytes[i], outs[j], out_bytes[j])) return FA_ERR_ARG;
+  const fa::host::Dims g{B, H, N, d, 2};
+  fa::host::Operand op[8];
+  for (int i = 0; i < 8; ++i) {
+    const int st = fa::host::make_operand(ptrs[i], strides ? strides + 3 * i : nullptr, g, &op[i], &plan->view[i]);
+    if (st != FA_OK) return st;
   }
+  // Outputs: each gradient is free of self-overlap and shares no byte with
+  // another operand; delta shares none with anything.
+  const long long rb = (long long)B * H * N * (long long)sizeof(float);
+  for (int i = 5; i < 8; ++i) {
+    if (!fa::host::self_disjoint(op[i], g)) return FA_ERR_ARG;
+    for (int j = 0; j < 8; ++j)
+      if (j != i && !fa::host::disjoint(op[i], op[j], g)) return FA_ERR_ARG;
+    if (fa::host::ranges_overlap((uintptr_t)lse, rb, op[i].p, op[i].span)) return FA_ERR_ARG;
+  }
+  for (int j = 0; j < 8; ++j)
+    if (fa::host::ranges_overlap((uintptr_t)delta, rb, op[j].p, op[j].span)) return FA_ERR_ARG;
+  if (fa::host::ranges_overlap((uintptr_t)delta, rb, (uintptr_t)lse, rb)) return FA_ERR_ARG;
+  return FA_OK;
+}
+
+}  // namespace
+
+extern "C" int fa_bwd_strided_check(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                                    const void* dout, void* dq, void* dk, void* dv, float* delta,
+                                    const long long* strides, int B, int H, int N, int d, float scale,
+                                    int causal, int window_left, int window_right, int dtype) {
+  BwdPlan plan;
+  return plan_bwd(q, k, v, o, lse, dout, dq, dk, dv, delta, strides, B, H, N, d, scale, causal, window_left,
+                  window_right, dtype, &plan);
+}
+
+extern "C" int fa_bwd_strided(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                              const void* dout, void* dq, void* dk, void* dv, float* delta,
+                              const long long* strides, int B, int H, int N, int d, float scale, int causal,
+                              int window_left, int window_right, int dtype, void* stream) {
+  BwdPlan plan;
+  const int status = plan_bwd(q, k, v, o, lse, dout, dq, dk, dv, delta, strides, B, H, N, d, scale, causal,
+                              window_left, window_right, dtype, &plan);
+  if (status != FA_OK || plan.blocks == 0) return status;
+  const long long tiles = plan.tiles, blocks = plan.blocks;
+  fa::View* const view = plan.view;
 
   const void* kd;
   const void* kq;
@@ -686,9 +700,12 @@ extern "C" int fa_bwd(const void* q, const void* k, const void* v, const void* o
   }
   hipStream_t st = (hipStream_t)stream;
 
-  long long nrows = (long long)rows;
-  void* dargs[] = {(void*)&o, (void*)&dout, (void*)&delta, (void*)&nrows};
-  const long long dblocks = ((long long)rows + rpb - 1) / rpb;
+  const long long rows = (long long)B * H * N;
+  int h_arg = H, n_arg = N;
+  long long nrows = rows;
+  void* dargs[] = {(void*)&o, (void*)&dout, (void*)&delta, (void*)&view[3], (void*)&view[4],
+                   (void*)&h_arg, (void*)&n_arg, (void*)&nrows};
+  const long long dblocks = (rows + rpb - 1) / rpb;
   if (dblocks > INT_MAX) return FA_ERR_SHAPE;
   if (hipLaunchKernel(kd, dim3((unsigned)dblocks), dim3(fa::kThreads), dargs, 0, st) != hipSuccess)
     return FA_ERR_LAUNCH;
@@ -699,16 +716,28 @@ extern "C" int fa_bwd(const void* q, const void* k, const void* v, const void* o
   if (causal) wr = 0;
   float c = (float)((double)scale * 1.4426950408889634074);
   float sc = scale;
-  int n_arg = N, nt = (int)tiles, nb = (int)blocks;
+  int nt = (int)tiles, nb = (int)blocks;
   const float* delta_c = delta;
-  void* qargs[] = {(void*)&q, (void*)&k, (void*)&v, (void*)&dout, (void*)&lse, (void*)&delta_c, (void*)&dq,
-                   (void*)&n_arg, (void*)&nt, (void*)&nb, (void*)&c, (void*)&sc, (void*)&wl, (void*)&wr};
+  void* qargs[] = {(void*)&q,       (void*)&k,       (void*)&v,       (void*)&dout,    (void*)&lse,
+                   (void*)&delta_c, (void*)&dq,      (void*)&view[0], (void*)&view[1], (void*)&view[2],
+                   (void*)&view[4], (void*)&view[5], (void*)&h_arg,   (void*)&n_arg,   (void*)&nt,
+                   (void*)&nb,      (void*)&c,       (void*)&sc,      (void*)&wl,      (void*)&wr};
   if (hipLaunchKernel(kq, dim3((unsigned)blocks), dim3(fa::kThreads), qargs, 0, st) != hipSuccess)
     return FA_ERR_LAUNCH;
-  void* kargs[] = {(void*)&q, (void*)&k, (void*)&v, (void*)&dout, (void*)&lse, (void*)&delta_c, (void*)&dk,
-                   (void*)&dv, (void*)&n_arg, (void*)&nt, (void*)&nb, (void*)&c, (void*)&sc, (void*)&wl,
-                   (void*)&wr};
+  void* kargs[] = {(void*)&q,       (void*)&k,       (void*)&v,       (void*)&dout,    (void*)&lse,
+                   (void*)&delta_c, (void*)&dk,      (void*)&dv,      (void*)&view[0], (void*)&view[1],
+                   (void*)&view[2], (void*)&view[4], (void*)&view[6], (void*)&view[7], (void*)&h_arg,
+                   (void*)&n_arg,   (void*)&nt,      (void*)&nb,      (void*)&c,       (void*)&sc,
+                   (void*)&wl,      (void*)&wr};
   if (hipLaunchKernel(kkv, dim3((unsigned)blocks), dim3(fa::kThreads), kargs, 0, st) != hipSuccess)
     return FA_ERR_LAUNCH;
   return FA_OK;
+}
+
+extern "C" int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                      const void* dout, void* dq, void* dk, void* dv, float* delta, int B, int H, int N,
+                      int d, float scale, int causal, int window_left, int window_right, int dtype,
+                      void* stream) {
+  return fa_bwd_strided(q, k, v, o, lse, dout, dq, dk, dv, delta, nullptr, B, H, N, d, scale, causal,
+                        window_left, window_right, dtype, stream);
 }

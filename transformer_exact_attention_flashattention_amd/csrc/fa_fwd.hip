@@ -8,14 +8,15 @@
 #include <cstdint>
 
 #include "fa.h"
+#include "fa_host.h"
 #include "fa_kernels.h"
 
 namespace {
 
-typedef void (*fwd16_fn)(const uint16_t*, const uint16_t*, const uint16_t*, uint16_t*, float*, int, int,
-                         int, float, int, int);
-typedef void (*fwd32_fn)(const float*, const float*, const float*, float*, float*, int, int, int,
-                         float, int, int);
+typedef void (*fwd16_fn)(const uint16_t*, const uint16_t*, const uint16_t*, uint16_t*, float*, fa::View,
+                         fa::View, fa::View, fa::View, int, int, int, int, float, int, int);
+typedef void (*fwd32_fn)(const float*, const float*, const float*, float*, float*, fa::View, fa::View,
+                         fa::View, fa::View, int, int, int, int, float, int, int);
 
 template <class T>
 fwd16_fn pick16(int d, bool causal) {
@@ -57,11 +58,6 @@ int check_shape(int B, int H, int N, int d, int causal, int dtype, long long* nb
   return FA_OK;
 }
 
-bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
-  const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
-  return x < y + nb && y < x + na;
-}
-
 }  // namespace
 
 extern "C" const char* fa_strerror(int status) {
@@ -71,9 +67,11 @@ extern "C" const char* fa_strerror(int status) {
     case FA_ERR_SHAPE: return "a size is negative or too large";
     case FA_ERR_HEADDIM: return "head dimension must be 64, 128 or 256";
     case FA_ERR_DTYPE: return "dtype must be FA_F16, FA_BF16 or FA_F32";
-    case FA_ERR_ALIGN: return "q, k, v, o must be 16-byte aligned and lse 4-byte aligned";
+    case FA_ERR_ALIGN:
+      return "q, k, v, o (and every row of their views) must be 16-byte aligned and lse 4-byte aligned";
     case FA_ERR_ARG:
-      return "causal must be 0 or 1, scale finite, window sides >= -1, and o/lse must not overlap q/k/v";
+      return "causal must be 0 or 1, scale finite, window sides >= -1, and outputs must not overlap "
+             "inputs, each other or themselves";
     case FA_ERR_LAUNCH: return "the HIP runtime rejected the kernel launch";
   }
   return "unknown fa_status";
@@ -90,33 +88,63 @@ extern "C" int fa_fwd_grid(int B, int H, int N, int d, int causal, int dtype, lo
   return FA_OK;
 }
 
-extern "C" int fa_fwd_window(const void* q, const void* k, const void* v, void* o, float* lse, int B,
-                             int H, int N, int d, float scale, int causal, int window_left,
-                             int window_right, int dtype, void* stream) {
+namespace {
+
+// Everything fa_fwd_strided checks, without a HIP call. On FA_OK, nblocks
+// is the launch size (0: nothing to do) and view the kernels' operands.
+struct FwdPlan {
   long long nblocks = 0;
   int nqt = 0;
-  int st = check_shape(B, H, N, d, causal, dtype, &nblocks, &nqt);
+  fa::View view[4];
+};
+
+int plan_fwd(const void* q, const void* k, const void* v, void* o, float* lse, const long long* strides, int B,
+             int H, int N, int d, float scale, int causal, int window_left, int window_right, int dtype,
+             FwdPlan* plan) {
+  int st = check_shape(B, H, N, d, causal, dtype, &plan->nblocks, &plan->nqt);
   if (st != FA_OK) return st;
   if (!std::isfinite(scale)) return FA_ERR_ARG;
   if (window_left < -1 || window_right < -1) return FA_ERR_ARG;
-  if (nblocks == 0) return FA_OK;  // B*H*N == 0: nothing to do
+  if (plan->nblocks == 0) return FA_OK;  // B*H*N == 0: nothing to do
   if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
-  if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o) & 15) return FA_ERR_ALIGN;
   if ((uintptr_t)lse & 3) return FA_ERR_ALIGN;
 
-  const size_t esz = dtype == FA_F32 ? 4 : 2;
-  const size_t elems = (size_t)B * H * N * d;
-  const size_t tbytes = elems * esz;
-  const size_t lbytes = (size_t)B * H * N * sizeof(float);
-  const void* ins[3] = {q, k, v};
-  for (const void* in : ins) {
-    if (overlaps(o, tbytes, in, tbytes) || overlaps(lse, lbytes, in, tbytes)) return FA_ERR_ARG;
+  const fa::host::Dims g{B, H, N, d, dtype == FA_F32 ? 4 : 2};
+  const void* ptrs[4] = {q, k, v, o};
+  fa::host::Operand op[4];
+  for (int i = 0; i < 4; ++i) {
+    st = fa::host::make_operand(ptrs[i], strides ? strides + 3 * i : nullptr, g, &op[i], &plan->view[i]);
+    if (st != FA_OK) return st;
   }
-  if (overlaps(o, tbytes, lse, lbytes)) return FA_ERR_ARG;
+  const long long lbytes = (long long)B * H * N * (long long)sizeof(float);
+  if (!fa::host::self_disjoint(op[3], g)) return FA_ERR_ARG;
+  for (int i = 0; i < 3; ++i)
+    if (!fa::host::disjoint(op[3], op[i], g)) return FA_ERR_ARG;
+  for (int i = 0; i < 4; ++i)
+    if (fa::host::ranges_overlap((uintptr_t)lse, lbytes, op[i].p, op[i].span)) return FA_ERR_ARG;
+  return FA_OK;
+}
+
+}  // namespace
+
+extern "C" int fa_fwd_strided_check(const void* q, const void* k, const void* v, void* o, float* lse,
+                                    const long long* strides, int B, int H, int N, int d, float scale,
+                                    int causal, int window_left, int window_right, int dtype) {
+  FwdPlan plan;
+  return plan_fwd(q, k, v, o, lse, strides, B, H, N, d, scale, causal, window_left, window_right, dtype, &plan);
+}
+
+extern "C" int fa_fwd_strided(const void* q, const void* k, const void* v, void* o, float* lse,
+                              const long long* strides, int B, int H, int N, int d, float scale, int causal,
+                              int window_left, int window_right, int dtype, void* stream) {
+  FwdPlan plan;
+  const int st =
+      plan_fwd(q, k, v, o, lse, strides, B, H, N, d, scale, causal, window_left, window_right, dtype, &plan);
+  if (st != FA_OK || plan.nblocks == 0) return st;
 
   // log2(e) is folded into the scale: exp(x * scale) == exp2(x * c).
   const float c = (float)((double)scale * 1.4426950408889634074);
-  int n_arg = N, nqt_arg = nqt, nb_arg = (int)nblocks;
+  int h_arg = H, n_arg = N, nqt_arg = plan.nqt, nb_arg = (int)plan.nblocks;
   float c_arg = c;
   // Visible keys of query i: i - wl .. i + wr, an unbounded side as 2^30
   // (N is below 2^30, so no sum of a row index and a side overflows).
@@ -124,8 +152,11 @@ extern "C" int fa_fwd_window(const void* q, const void* k, const void* v, void* 
   int wl = window_left < 0 ? kUnbounded : window_left;
   int wr = window_right < 0 ? kUnbounded : window_right;
   if (causal) wr = 0;
-  void* args[] = {(void*)&q, (void*)&k, (void*)&v, (void*)&o, (void*)&lse, (void*)&n_arg,
-                  (void*)&nqt_arg, (void*)&nb_arg, (void*)&c_arg, (void*)&wl, (void*)&wr};
+  fa::View* const view = plan.view;
+  void* args[] = {(void*)&q,       (void*)&k,       (void*)&v,       (void*)&o,     (void*)&lse,
+                  (void*)&view[0], (void*)&view[1], (void*)&view[2], (void*)&view[3], (void*)&h_arg,
+                  (void*)&n_arg,   (void*)&nqt_arg, (void*)&nb_arg,  (void*)&c_arg, (void*)&wl,
+                  (void*)&wr};
 
   const void* fn = nullptr;
   if (dtype == FA_F32) {
@@ -136,9 +167,16 @@ extern "C" int fa_fwd_window(const void* q, const void* k, const void* v, void* 
     fn = (const void*)pick16<fa::F16>(d, causal != 0);
   }
   if (!fn) return FA_ERR_HEADDIM;
-  const hipError_t e = hipLaunchKernel(fn, dim3((unsigned)nblocks), dim3(fa::kThreads), args, 0,
+  const hipError_t e = hipLaunchKernel(fn, dim3((unsigned)plan.nblocks), dim3(fa::kThreads), args, 0,
                                        (hipStream_t)stream);
   return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+extern "C" int fa_fwd_window(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                             int H, int N, int d, float scale, int causal, int window_left,
+                             int window_right, int dtype, void* stream) {
+  return fa_fwd_strided(q, k, v, o, lse, nullptr, B, H, N, d, scale, causal, window_left, window_right, dtype,
+                        stream);
 }
 
 extern "C" int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,

@@ -81,6 +81,22 @@ struct F16 {
   }
 };
 
+// Element strides of one [B, H, N, d] operand whose d elements are
+// contiguous: batch, head and row (sequence position). A contiguous tensor
+// has (H N d, N d, d); a head-interleaved one such as the q slice of a packed
+// [B, N, 3, H, d] tensor has (3 N H d, d, 3 H d). The host guarantees that
+// every row start is 16-byte aligned and that 64 row strides fit in 32 bits.
+struct View {
+  long long b, h;
+  int r;
+};
+
+// Element offset of head bh = b * H + h.
+__device__ __forceinline__ long long view_base(const View& v, int bh, int H) {
+  const int b = bh / H;
+  return (long long)b * v.b + (long long)(bh - b * H) * v.h;
+}
+
 // Floor of a / b for b > 0 and any sign of a.
 __device__ __forceinline__ int floor_div(int a, int b) { return a >= 0 ? a / b : -((b - 1 - a) / b); }
 
@@ -179,13 +195,13 @@ __device__ __forceinline__ float online_softmax(f32x16& s, float c, int kb, int 
 // immediate offsets. Tiles are copied by buffer_load_dwordx4 ... lds: each
 // wave instruction fills 1 KiB of LDS, 16 bytes per lane in lane order, and
 // each lane fetches the global chunk that belongs at its slot (pad slots
-// fetch a duplicate of a real chunk). Rows past the end of the sequence
-// fetch the last real row instead (their scores are masked, and the
-// duplicate keeps V finite).
+// fetch a duplicate of a real chunk). Global rows are any 16-byte multiple
+// apart (the row stride of the operand's view), so a head of a packed
+// tensor is read in place.
 
 template <int D>
 struct Geo16 {
-  static constexpr int kRowB = 2 * D;         // bytes of one K/V row in memory
+  static constexpr int kRowB = 2 * D;         // bytes of one K/V row's values
   static constexpr int kSK = kRowB + 16;      // LDS K row stride
   static constexpr int kSV = kRowB + 64;      // LDS V row stride
   // LDS bytes of a K (V) tile, rounded up to whole 4 KiB so that each of the
@@ -197,17 +213,18 @@ struct Geo16 {
   static constexpr int kVPW = kVT / 4096;
 };
 
-// Source byte offset (relative to the tile's first row) of LDS slot t of a
-// tile whose rows are STRIDE bytes apart: pad slots and filler past the 64
-// rows fetch a real chunk again (their LDS bytes are never read).
+// Source byte offset (relative to the tile's first row, global rows rs
+// bytes apart) of LDS slot t of a tile whose LDS rows are STRIDE bytes
+// apart: pad slots and filler past the 64 rows fetch a real chunk again
+// (their LDS bytes are never read).
 template <int D, int STRIDE>
-__device__ __forceinline__ uint32_t tile_src(int t) {
+__device__ __forceinline__ uint32_t tile_src(int t, int rs) {
   constexpr int R = STRIDE / 16;  // 16-byte slots per LDS row
   const int m = t / R;
   int q = t - m * R;
   if (q >= D / 8) q = 0;  // pad slot
   if (m >= kBc) return 0;  // filler
-  return (uint32_t)(m * 2 * D + 16 * q);
+  return (uint32_t)m * (uint32_t)rs + (uint32_t)(16 * q);
 }
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
@@ -251,21 +268,22 @@ constexpr float kTauPow = 256.0f;  // 2^kTau
 constexpr uint32_t kBufWord3 = 0x00020000u;  // raw buffer, 32-bit data format
 
 // Copies one tile (its first row at `src`, `nvalid` rows of the sequence
-// left from there) into LDS at `dst`: wave w issues copy blocks w, w + 4, ...
-// of the 1 KiB blocks; off[i] is the lane's source offset for its i-th
-// block. The buffer's range is the tile's valid rows, so in a ragged last
-// tile the lanes past the end load zeros. No branches: the copies can be
-// interleaved with matrix-core work.
+// left from there, rows rs >= 2D bytes apart) into LDS at `dst`: wave w
+// issues copy blocks w, w + 4, ... of the 1 KiB blocks; off[i] is the lane's
+// source offset for its i-th block. The buffer's range ends with the last
+// valid row's values, so in a ragged last tile the lanes past the end load
+// zeros. No branches: the copies can be interleaved with matrix-core work.
 template <int D, int NPW>
-__device__ __forceinline__ void copy_tile(const unsigned char* src, int nvalid, unsigned char* dst,
+__device__ __forceinline__ void copy_tile(const unsigned char* src, int nvalid, int rs, unsigned char* dst,
                                           const uint32_t (&off)[NPW], int wave) {
 #if defined(__HIP_DEVICE_COMPILE__)  // buffer resources exist only on the device side
   const int rows = nvalid < kBc ? nvalid : kBc;
-  const __amdgpu_buffer_rsrc_t rs =
-      __builtin_amdgcn_make_buffer_rsrc((void*)src, (short)0, rows * 2 * D, kBufWord3);
+  const int range = rows > 0 ? (rows - 1) * rs + 2 * D : 0;
+  const __amdgpu_buffer_rsrc_t rs_ =
+      __builtin_amdgcn_make_buffer_rsrc((void*)src, (short)0, range, kBufWord3);
 #pragma unroll
   for (int i = 0; i < NPW; ++i)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, as_lds(dst + 1024 * (wave + 4 * i)), 16, off[i], 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_, as_lds(dst + 1024 * (wave + 4 * i)), 16, off[i], 0, 0, 0);
 #endif
 }
 
@@ -302,7 +320,8 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
                           amdgpu_waves_per_eu(D >= 256 ? 1 : 2, D >= 256 ? 1 : 2)))
 void fwd16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                   const uint16_t* __restrict__ V, uint16_t* __restrict__ O,
-                  float* __restrict__ LSE, int N, int nqt, int nblocks, float c, int wl, int wr) {
+                  float* __restrict__ LSE, View vq, View vk, View vv, View vo, int H, int N, int nqt,
+                  int nblocks, float c, int wl, int wr) {
   using G = Geo16<D>;
   typedef short s16x4 __attribute__((ext_vector_type(4)));
   typedef __attribute__((address_space(3))) s16x4* lds_s16x4_t;
@@ -313,12 +332,12 @@ void fwd16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K
 
   int bh, qt;
   decode_block(nblocks, nqt, CAUSAL, bh, qt);
-  const size_t base = (size_t)bh * (size_t)N * D;
-  Q += base;
-  O += base;
+  Q += view_base(vq, bh, H);
+  O += view_base(vo, bh, H);
   LSE += (size_t)bh * N;
-  const unsigned char* const kg = (const unsigned char*)(K + base);
-  const unsigned char* const vg = (const unsigned char*)(V + base);
+  const unsigned char* const kg = (const unsigned char*)(K + view_base(vk, bh, H));
+  const unsigned char* const vg = (const unsigned char*)(V + view_base(vv, bh, H));
+  const int ksb = 2 * vk.r, vsb = 2 * vv.r;  // K and V row strides, bytes
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -338,7 +357,7 @@ void fwd16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K
   u32x4 qf[D / 16];
 #pragma unroll
   for (int s = 0; s < D / 16; ++s) {
-    qf[s] = qrow < N ? *(const u32x4*)(Q + (size_t)qrow * D + 16 * s + 8 * hh) : u32x4{0, 0, 0, 0};
+    qf[s] = qrow < N ? *(const u32x4*)(Q + (long long)qrow * vq.r + 16 * s + 8 * hh) : u32x4{0, 0, 0, 0};
     qf[s] ^= qflip;
   }
 
@@ -354,9 +373,9 @@ void fwd16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K
   // Tile-invariant source offsets of this lane's copy slots.
   uint32_t koff[G::kKPW], voff[G::kVPW];
 #pragma unroll
-  for (int i = 0; i < G::kKPW; ++i) koff[i] = tile_src<D, G::kSK>(64 * (wave + 4 * i) + lane);
+  for (int i = 0; i < G::kKPW; ++i) koff[i] = tile_src<D, G::kSK>(64 * (wave + 4 * i) + lane, ksb);
 #pragma unroll
-  for (int i = 0; i < G::kVPW; ++i) voff[i] = tile_src<D, G::kSV>(64 * (wave + 4 * i) + lane);
+  for (int i = 0; i < G::kVPW; ++i) voff[i] = tile_src<D, G::kSV>(64 * (wave + 4 * i) + lane, vsb);
 
   // With a ragged last tile, the copy of its rows past the end may leave old
   // LDS contents in place; starting from zeros keeps every value read finite
@@ -375,10 +394,10 @@ void fwd16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K
   }
 
   auto issue_k = [&](int kt, unsigned char* dst) {
-    copy_tile<D, G::kKPW>(kg + (size_t)kt * kBc * G::kRowB, N - kt * kBc, dst, koff, wave);
+    copy_tile<D, G::kKPW>(kg + (long long)(kt * kBc) * ksb, N - kt * kBc, ksb, dst, koff, wave);
   };
   auto issue_v = [&](int kt, unsigned char* dst) {
-    copy_tile<D, G::kVPW>(vg + (size_t)kt * kBc * G::kRowB, N - kt * kBc, dst, voff, wave);
+    copy_tile<D, G::kVPW>(vg + (long long)(kt * kBc) * vsb, N - kt * kBc, vsb, dst, voff, wave);
   };
 
   // Per-lane LDS read bases. K: MFMA row n holds key sigma(n) (second tile:
@@ -598,7 +617,7 @@ void fwd16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K
   const float l_tot = pair_sum(l_run);
   const float inv = 1.0f / l_tot;
   if (qrow < N) {
-    uint16_t* orow = O + (size_t)qrow * D;
+    uint16_t* orow = O + (long long)qrow * vo.r;
 #pragma unroll
     for (int t = 0; t < D / 32; ++t) {
 #pragma unroll
@@ -634,7 +653,8 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
                           amdgpu_waves_per_eu(1, 1)))
 void fwd32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
                   const float* __restrict__ V, float* __restrict__ O,
-                  float* __restrict__ LSE, int N, int nqt, int nblocks, float c, int wl, int wr) {
+                  float* __restrict__ LSE, View vq, View vk, View vv, View vo, int H, int N, int nqt,
+                  int nblocks, float c, int wl, int wr) {
   constexpr int DCH = D / 4;                  // 16-byte chunks per row
   constexpr int VSTRIDE = D + 8;              // floats per padded V row
   constexpr int KS_BYTES = kBc * D * 4;
@@ -651,11 +671,10 @@ void fwd32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
 
   int bh, qt;
   decode_block(nblocks, nqt, CAUSAL, bh, qt);
-  const size_t base = (size_t)bh * (size_t)N * D;
-  Q += base;
-  K += base;
-  V += base;
-  O += base;
+  Q += view_base(vq, bh, H);
+  K += view_base(vk, bh, H);
+  V += view_base(vv, bh, H);
+  O += view_base(vo, bh, H);
   LSE += (size_t)bh * N;
 
   const int tid = threadIdx.x;
@@ -672,7 +691,7 @@ void fwd32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
   f32x4 qf[D / 8];
 #pragma unroll
   for (int u = 0; u < D / 8; ++u)
-    qf[u] = qrow < N ? *(const f32x4*)(Q + (size_t)qrow * D + 8 * u + 4 * hh) : f32x4{0, 0, 0, 0};
+    qf[u] = qrow < N ? *(const f32x4*)(Q + (long long)qrow * vq.r + 8 * u + 4 * hh) : f32x4{0, 0, 0, 0};
 
   // Key tiles the block needs (query i sees keys i - wl .. i + wr; wr is 0
   // when causal, an unbounded side is 2^30).
@@ -689,8 +708,8 @@ void fwd32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
       const int g = tid + i * kThreads;
       const int key = g / DCH, ch = g % DCH;
       const bool ok = k0 + key < N;
-      kreg[i] = ok ? *(const f32x4*)(K + (size_t)(k0 + key) * D + ch * 4) : f32x4{0, 0, 0, 0};
-      vreg[i] = ok ? *(const f32x4*)(V + (size_t)(k0 + key) * D + ch * 4) : f32x4{0, 0, 0, 0};
+      kreg[i] = ok ? *(const f32x4*)(K + (long long)(k0 + key) * vk.r + ch * 4) : f32x4{0, 0, 0, 0};
+      vreg[i] = ok ? *(const f32x4*)(V + (long long)(k0 + key) * vv.r + ch * 4) : f32x4{0, 0, 0, 0};
     }
   };
   auto swrite_regs = [&]() {
@@ -709,10 +728,10 @@ void fwd32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
       const int g = tid + i * kThreads;
       const int key = g / DCH, ch = g % DCH;
       const bool ok = k0 + key < N;
-      const f32x4 kv = ok ? *(const f32x4*)(K + (size_t)(k0 + key) * D + ch * 4) : f32x4{0, 0, 0, 0};
-      const f32x4 vv = ok ? *(const f32x4*)(V + (size_t)(k0 + key) * D + ch * 4) : f32x4{0, 0, 0, 0};
-      *(f32x4*)(ks + key * (D * 4) + ((ch ^ (key & 7)) << 4)) = kv;
-      *(f32x4*)(vs + key * VSTRIDE + ch * 4) = vv;
+      const f32x4 kx = ok ? *(const f32x4*)(K + (long long)(k0 + key) * vk.r + ch * 4) : f32x4{0, 0, 0, 0};
+      const f32x4 vx = ok ? *(const f32x4*)(V + (long long)(k0 + key) * vv.r + ch * 4) : f32x4{0, 0, 0, 0};
+      *(f32x4*)(ks + key * (D * 4) + ((ch ^ (key & 7)) << 4)) = kx;
+      *(f32x4*)(vs + key * VSTRIDE + ch * 4) = vx;
     }
   };
 
@@ -788,7 +807,7 @@ void fwd32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
   const float l_tot = wave_pair_sum(l_run);
   const float inv = 1.0f / l_tot;
   if (qrow < N) {
-    float* orow = O + (size_t)qrow * D;
+    float* orow = O + (long long)qrow * vo.r;
 #pragma unroll
     for (int t = 0; t < D / 32; ++t) {
 #pragma unroll
