@@ -194,9 +194,12 @@ def bench_packed(fa, inputs, dev, stream, steps, warmup):
     def contiguous():
         fa.fwd(*dst, causal=c["causal"], out=oc, lse=lsec)
 
-    _, per_s = time_launches(strided, stream, steps, warmup)
-    _, per_u = time_launches(unpack, stream, steps, warmup)
-    _, per_c = time_launches(contiguous, stream, steps, warmup)
+    # Two alternating rounds, so that both calls see the same clock state.
+    per_s, per_u, per_c = [], [], []
+    for _ in range(2):
+        per_c += time_launches(contiguous, stream, steps, warmup)[1]
+        per_s += time_launches(strided, stream, steps, warmup)[1]
+        per_u += time_launches(unpack, stream, steps, warmup)[1]
     torch.cuda.synchronize()
     same = bool(torch.equal(o.transpose(1, 2), oc)) and bool(torch.equal(lse, lsec))
     log(f"[bench] packed: strided == contiguous bitwise: {same}")
