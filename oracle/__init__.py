@@ -19,7 +19,9 @@ Sources (the web pages this work is built from):
 * [P1] "Compiling Flash Attention 2.8.3 on Windows with an RTX 3090"
   (intelliparadigm.com): section 5.2 / 10.1 (``softmax_scale=None`` means
   1/sqrt(d); ``causal`` flag; ``window_size`` local-attention window);
-  section 9.2 item 2 (the backward recomputes instead of storing).
+  section 9.2 item 2 (the backward recomputes instead of storing); section
+  11.2 (inference over long contexts, the use of split-KV partial results
+  and their merge).
 
 Parity status: every public function here is pinned by CPU tests (brute force
 in 40-digit decimal arithmetic, closed forms, invariants, a hand-derived
@@ -35,3 +37,4 @@ from .attention import (  # noqa: F401
 )
 from .backward import attention_bwd_ref  # noqa: F401
 from .bruteforce import attention_bruteforce  # noqa: F401
+from .splitkv import merge_ref, partial_ref  # noqa: F401
