@@ -211,6 +211,53 @@ def bench_packed(fa, inputs, dev, stream, steps, warmup):
             "parity_ok": same, "parity": "bitwise equal to the contiguous call on unpacked copies"}
 
 
+def bench_splitkv(fa, inputs, dev, stream, steps, warmup, no_parity):
+    """A low-occupancy shape, one long causal head (B=1, H=1, N=16384,
+    d=128, bf16: 128 query tiles for 256 compute units): the plain grid
+    beside split-KV with the library's choice of parts (fwd kernel + merge,
+    timed together). Parity of the split result on sampled rows."""
+    import numpy as np
+    import torch
+
+    B, H, N, D = 1, 1, 16384, 128
+    log(f"[bench] split-KV on B={B} H={H} N={N} d={D} causal: inputs")
+    q, k, v = inputs.make_qkv(B, H, N, D, "bf16", seed=42)
+    qd, kd, vd = (t.to(dev) for t in (q, k, v))
+    o = torch.empty_like(qd)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    splits = fa.splitkv_num_splits(B, H, N, D, True, dtype=fa.FA_BF16)
+    ws = torch.empty(fa.splitkv_workspace_bytes(B, H, N, D, splits), dtype=torch.uint8, device=dev)
+
+    def plain():
+        fa.fwd(qd, kd, vd, causal=True, out=o, lse=lse, num_splits=1)
+
+    def split():
+        fa.fwd(qd, kd, vd, causal=True, out=o, lse=lse, num_splits=splits, workspace=ws)
+
+    ok, err_o, err_l = None, float("nan"), float("nan")
+    if not no_parity:
+        o.fill_(float("nan"))
+        split()
+        torch.cuda.synchronize()
+        rows = np.unique(np.concatenate([np.arange(64), np.random.default_rng(2).choice(N, 64, replace=False),
+                                         np.arange(N - 32, N)]))
+        err_o, err_l = check_parity(o.cpu(), lse.cpu(), q, k, v, 1.0 / math.sqrt(D), True, rows)
+        ok = err_o <= 1e-2 and err_l <= 1e-3 and bool(torch.isfinite(o).all())
+        log(f"[bench] split-KV: max|dO|={err_o:.3e} max|dLSE|={err_l:.3e} parity={'ok' if ok else 'FAIL'}")
+    per_p, per_s = [], []
+    for _ in range(2):
+        per_p += time_launches(plain, stream, steps, warmup)[1]
+        per_s += time_launches(split, stream, steps, warmup)[1]
+    kp, ks = float(np.mean(per_p)), float(np.mean(per_s))
+    flops = 4.0 * B * H * N * N * D / 2
+    return {"workload": "one long causal head, B=1 H=1 N=16384 d=128 bf16", "num_splits": splits,
+            "split_ms_mean": round(ks, 4), "plain_ms_mean": round(kp, 4), "speedup": round(kp / ks, 3),
+            "tflops": round(flops / (ks * 1e-3) / 1e12, 2),
+            "frac": round(flops / (ks * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "timed": "fwd kernel + merge kernel per call", "parity_ok": ok, "max_abs_dO": err_o,
+            "max_abs_dLSE": err_l}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -344,6 +391,7 @@ def main():
         out["backward"] = bench_backward(fa, inputs, dev, stream, max(args.steps, 10), args.warmup,
                                          args.no_parity)
         out["packed"] = bench_packed(fa, inputs, dev, stream, max(args.steps, 20), args.warmup)
+        out["splitkv"] = bench_splitkv(fa, inputs, dev, stream, max(args.steps, 20), args.warmup, args.no_parity)
     if args.calibrate_copy:
         log("[bench] copy calibration: 3 x 1 GiB device-to-device copy")
         src = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
@@ -356,7 +404,8 @@ def main():
         log(f"[bench] CPU baseline: fp64 oracle on {args.cpu_heads} head(s)")
         out["cpu_baseline"] = cpu_baseline(q, k, v, scale, True, args.cpu_heads)
     print(json.dumps(out), flush=True)
-    failed = [par["ok"]] + [out[k]["parity_ok"] for k in ("secondary", "fp32", "window", "backward", "packed")
+    failed = [par["ok"]] + [out[k]["parity_ok"] for k in ("secondary", "fp32", "window", "backward", "packed",
+                                                          "splitkv")
                           if k in out]
     if any(f is False for f in failed):
         sys.exit(1)

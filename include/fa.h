@@ -137,6 +137,59 @@ int fa_fwd_strided(const void* q, const void* k, const void* v, void* o, float* 
                    int causal, int window_left, int window_right, int dtype, void* stream);
 
 /*
+ * fa_fwd_splitkv - fa_fwd_strided with the key range of every query tile
+ * split into num_splits parts that run as separate workgroups, for shapes
+ * whose B * H * N gives too few workgroups to fill the GPU (small batches,
+ * few heads, short sequences). Each part writes its partial result over its
+ * keys, and a merge kernel combines them:
+ *   LSE = ln sum_s exp(LSE_s),   O = sum_s exp(LSE_s - LSE) O_s,
+ * where O_s and LSE_s are the attention output and LSE over the part's keys
+ * alone. This follows from the definition: the softmax over a union of
+ * disjoint key sets is the LSE-weighted mix of the softmaxes over each set.
+ * The use is the long-context inference of section 11.2 of the flash-attn
+ * 2.8.3 build guide (intelliparadigm.com); the pages give no procedure.
+ *
+ * num_splits  0: the library chooses (fa_fwd_num_splits); 1: no split (the
+ *             fa_fwd_strided kernel, workspace unused and may be NULL);
+ *             2 .. 64: that many parts. Part s of a query tile whose key
+ *             tiles (64 keys each) are t_0 .. t_0 + n - 1 covers tiles
+ *             t_0 + floor(n s / S) .. t_0 + floor(n (s + 1) / S) - 1.
+ * workspace   device pointer, 16-byte aligned, of at least
+ *             fa_fwd_splitkv_workspace(...) bytes, owned by the caller, not
+ *             overlapping any operand; written, its previous contents
+ *             ignored. Layout: the parts' O_s as float32 [S, B*H, N, d],
+ *             then their LSE_s as float32 [S, B*H, N] (a part with no
+ *             visible key of a row holds O_s = 0, LSE_s = -inf there).
+ * workspace_bytes  its size.
+ *
+ * The result equals fa_fwd_strided's up to rounding (the parts are kept in
+ * float32 and O is rounded once, in the merge). Two kernels are enqueued on
+ * stream in order. Other arguments and errors as fa_fwd_strided; in
+ * addition FA_ERR_ARG for num_splits outside 0 .. 64, a workspace that is
+ * too small or overlaps an operand, FA_ERR_NULL / FA_ERR_ALIGN for a
+ * missing or misaligned workspace when more than one part runs.
+ */
+int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse,
+                   const long long* strides, void* workspace, long long workspace_bytes,
+                   int num_splits, int B, int H, int N, int d, float scale, int causal,
+                   int window_left, int window_right, int dtype, void* stream);
+
+/*
+ * fa_fwd_num_splits - host-only: the number of parts fa_fwd_splitkv uses
+ * for num_splits = 0: 1 when the plain grid already fills half the GPU;
+ * otherwise enough parts to fill it, at most 16, while each part of the
+ * widest query tile keeps at least 16 key tiles (causal) or 32 (not
+ * causal). Writes it to *num_splits; returns the shape checks' status.
+ *
+ * fa_fwd_splitkv_workspace - host-only: the workspace bytes fa_fwd_splitkv
+ * needs for num_splits parts (0 for num_splits = 1): 4 * S * B * H * N *
+ * (d + 1). FA_ERR_ARG for num_splits outside 1 .. 64.
+ */
+int fa_fwd_num_splits(int B, int H, int N, int d, int causal, int window_left,
+                      int window_right, int dtype, int* num_splits);
+int fa_fwd_splitkv_workspace(int B, int H, int N, int d, int num_splits, long long* bytes);
+
+/*
  * fa_bwd - enqueue the backward pass: the gradients dq, dk, dv of a loss
  * whose gradient with respect to o is dout, for the forward pass fa_fwd_window
  * computed with the same q, k, v, scale, causal and window.

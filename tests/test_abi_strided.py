@@ -249,3 +249,44 @@ def test_bruteforce_soundness_of_overlap_rules():
         assert not self_overlaps(ptrs[3], strides[9:12], B, H, N, d, esz), f"trial {trial}: o overlaps itself"
     # the generator produces both outcomes in quantity
     assert accepted > 50 and rejected > 50, (accepted, rejected)
+
+
+# ------------------------------------------------------------- split-KV --
+
+def splitkv(ws, ws_bytes, splits, B=1, H=2, N=300, d=64):
+    ptrs = [0x100_0000, 0x200_0000, 0x300_0000, 0x400_0000]
+    return fa.fa_fwd_splitkv(*ptrs, 0x7000_0000, None, ws, ws_bytes, splits, B, H, N, d, 0.125, 0, -1, -1,
+                             fa.FA_BF16)
+
+
+def test_splitkv_workspace_size():
+    assert fa.splitkv_workspace_bytes(2, 3, 100, 128, 4) == 4 * 4 * 2 * 3 * 100 * 129
+    assert fa.splitkv_workspace_bytes(2, 3, 100, 128, 1) == 0
+    for bad in (0, 65, -1):
+        with pytest.raises(fa.FaError):
+            fa.splitkv_workspace_bytes(1, 1, 10, 64, bad)
+
+
+def test_splitkv_heuristic():
+    # large grids are not split
+    assert fa.splitkv_num_splits(1, 16, 16384, 256, True) == 1
+    assert fa.splitkv_num_splits(1, 128, 2048, 128, True) == 1
+    # one long head: split, at most 16 parts
+    s = fa.splitkv_num_splits(1, 1, 16384, 128, True)
+    assert 2 <= s <= 16
+    # every answer is within 1 .. 16 and 0 sizes give 1
+    assert fa.splitkv_num_splits(0, 4, 100, 64) == 1
+    for B, H, N, d in itertools.product((1, 2), (1, 3), (1, 65, 1000, 9000), (64, 128, 256)):
+        assert 1 <= fa.splitkv_num_splits(B, H, N, d, False) <= 16
+
+
+@pytest.mark.parametrize("ws,ws_bytes,splits,code", [
+    (0x5000_0000, 1 << 30, -1, ARG), (0x5000_0000, 1 << 30, 65, ARG),
+    (0, 1 << 30, 2, -1),                # no workspace
+    (0x5000_0008, 1 << 30, 2, ALIGN),   # misaligned workspace
+    (0x5000_0000, 1000, 2, ARG),        # too small
+    (0x200_0000 - 64, 1 << 30, 2, ARG),  # overlaps k
+    (0x7000_0000 - 256, 1 << 30, 3, ARG),  # overlaps lse
+])
+def test_splitkv_errors(ws, ws_bytes, splits, code):
+    assert splitkv(ws, ws_bytes, splits) == code

@@ -63,7 +63,8 @@ STATUS = {
 }
 # Every symbol include/fa.h declares.
 EXPORTS = ("fa_fwd", "fa_fwd_window", "fa_fwd_strided", "fa_bwd", "fa_bwd_strided", "fa_strerror",
-           "fa_fwd_grid", "fa_fwd_strided_check", "fa_bwd_strided_check")
+           "fa_fwd_grid", "fa_fwd_strided_check", "fa_bwd_strided_check", "fa_fwd_splitkv",
+           "fa_fwd_num_splits", "fa_fwd_splitkv_workspace")
 
 _lib = None
 
@@ -111,6 +112,16 @@ def lib() -> ctypes.CDLL:
             ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_float,
             ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
         ]
+        h.fa_fwd_splitkv.restype = ctypes.c_int
+        h.fa_fwd_splitkv.argtypes = [ctypes.c_void_p] * 5 + [
+            ctypes.POINTER(ctypes.c_longlong), ctypes.c_void_p, ctypes.c_longlong, ctypes.c_int,
+            ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_float,
+            ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+        ]
+        h.fa_fwd_num_splits.restype = ctypes.c_int
+        h.fa_fwd_num_splits.argtypes = [ctypes.c_int] * 8 + [ctypes.POINTER(ctypes.c_int)]
+        h.fa_fwd_splitkv_workspace.restype = ctypes.c_int
+        h.fa_fwd_splitkv_workspace.argtypes = [ctypes.c_int] * 5 + [ctypes.POINTER(ctypes.c_longlong)]
         h.fa_fwd_strided_check.restype = ctypes.c_int
         h.fa_fwd_strided_check.argtypes = h.fa_fwd_strided.argtypes[:-1]
         h.fa_bwd_strided_check.restype = ctypes.c_int
@@ -157,6 +168,32 @@ def fa_fwd_strided(q, k, v, o, lse, strides, B, H, N, d, scale, causal, window_l
     strides (batch, head, row of q, k, v, o) or is None (contiguous)."""
     return lib().fa_fwd_strided(q, k, v, o, lse, _strides_arg(strides, 12), B, H, N, d, scale, causal,
                                 window_left, window_right, dtype, stream)
+
+
+def fa_fwd_splitkv(q, k, v, o, lse, strides, workspace, workspace_bytes, num_splits, B, H, N, d, scale, causal,
+                   window_left, window_right, dtype, stream=None) -> int:
+    """Raw call of the split-KV entry point (strides as for fa_fwd_strided)."""
+    return lib().fa_fwd_splitkv(q, k, v, o, lse, _strides_arg(strides, 12), workspace, workspace_bytes, num_splits,
+                                B, H, N, d, scale, causal, window_left, window_right, dtype, stream)
+
+
+def splitkv_num_splits(B, H, N, d, causal=False, window_size=(-1, -1), dtype=FA_BF16):
+    """The number of key-range parts fa_fwd_splitkv picks by itself."""
+    left, right = _window(window_size)
+    n = ctypes.c_int(0)
+    st = lib().fa_fwd_num_splits(B, H, N, d, int(bool(causal)), left, right, dtype, ctypes.byref(n))
+    if st != 0:
+        raise FaError(st, strerror(st))
+    return n.value
+
+
+def splitkv_workspace_bytes(B, H, N, d, splits):
+    """Workspace bytes fa_fwd_splitkv needs for ``splits`` parts."""
+    n = ctypes.c_longlong(0)
+    st = lib().fa_fwd_splitkv_workspace(B, H, N, d, splits, ctypes.byref(n))
+    if st != 0:
+        raise FaError(st, strerror(st))
+    return n.value
 
 
 def fa_fwd_strided_check(q, k, v, o, lse, strides, B, H, N, d, scale, causal, window_left, window_right,
@@ -253,11 +290,15 @@ def _strides(*ts):
     return out
 
 
-def fwd(q, k, v, softmax_scale=None, causal=False, window_size=(-1, -1), out=None, lse=None):
+def fwd(q, k, v, softmax_scale=None, causal=False, window_size=(-1, -1), out=None, lse=None, num_splits=1,
+        workspace=None):
     """Attention forward on the GPU: returns (o [B,H,N,d], lse [B,H,N] fp32).
 
     q, k, v (and ``out`` if given) may be strided views; a new ``out`` is
-    contiguous."""
+    contiguous. ``num_splits`` > 1 splits every query tile's keys into that
+    many parts merged by log-sum-exp (fa_fwd_splitkv); 0 lets the library
+    choose; the workspace (a GPU tensor of at least
+    ``splitkv_workspace_bytes`` bytes) is allocated when not given."""
     import torch
 
     left, right = _window(window_size)
@@ -275,12 +316,27 @@ def fwd(q, k, v, softmax_scale=None, causal=False, window_size=(-1, -1), out=Non
         lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
     _check_view("out", out, q.shape, q.dtype, q.device)
     _check_rowstat("lse", lse, B, H, N, q.device)
+    splits = int(num_splits)
+    if splits == 0:
+        splits = splitkv_num_splits(B, H, N, d, causal, (left, right), code)
     with torch.cuda.device(q.device):
         stream = torch.cuda.current_stream().cuda_stream
-        st = fa_fwd_strided(
-            q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), _strides(q, k, v, out),
-            B, H, N, d, scale, int(bool(causal)), left, right, code, stream,
-        )
+        if splits == 1:
+            st = fa_fwd_strided(
+                q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), _strides(q, k, v, out),
+                B, H, N, d, scale, int(bool(causal)), left, right, code, stream,
+            )
+        else:
+            need = splitkv_workspace_bytes(B, H, N, d, splits)
+            if workspace is None:
+                workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+            if not workspace.is_cuda or workspace.device != q.device:
+                raise ValueError("workspace must be on q's device")
+            st = fa_fwd_splitkv(
+                q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), _strides(q, k, v, out),
+                workspace.data_ptr(), workspace.numel() * workspace.element_size(), splits,
+                B, H, N, d, scale, int(bool(causal)), left, right, code, stream,
+            )
     if st != 0:
         raise FaError(st, strerror(st))
     return out, lse

@@ -3,6 +3,7 @@
 // include/fa.h; the kernels are in fa_kernels.h.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <climits>
 #include <cmath>
 #include <cstdint>
@@ -14,9 +15,9 @@
 namespace {
 
 typedef void (*fwd16_fn)(const uint16_t*, const uint16_t*, const uint16_t*, uint16_t*, float*, fa::View,
-                         fa::View, fa::View, fa::View, int, int, int, int, float, int, int);
+                         fa::View, fa::View, fa::View, int, int, int, int, float, int, int, fa::SplitOut);
 typedef void (*fwd32_fn)(const float*, const float*, const float*, float*, float*, fa::View, fa::View,
-                         fa::View, fa::View, int, int, int, int, float, int, int);
+                         fa::View, fa::View, int, int, int, int, float, int, int, fa::SplitOut);
 
 template <class T>
 fwd16_fn pick16(int d, bool causal) {
@@ -36,6 +37,18 @@ fwd32_fn pick32(int d, bool causal) {
   }
   return nullptr;
 }
+
+template <class T>
+const void* pick_merge(int d) {
+  switch (d) {
+    case 64: return (const void*)fa::merge_kernel<T, 64>;
+    case 128: return (const void*)fa::merge_kernel<T, 128>;
+    case 256: return (const void*)fa::merge_kernel<T, 256>;
+  }
+  return nullptr;
+}
+
+constexpr int kMaxSplits = 64;
 
 // Query rows per workgroup of the kernel that serves dtype.
 int rows_per_block(int dtype) { return dtype == FA_F32 ? fa::kBr32 : fa::kBr; }
@@ -134,14 +147,44 @@ extern "C" int fa_fwd_strided_check(const void* q, const void* k, const void* v,
   return plan_fwd(q, k, v, o, lse, strides, B, H, N, d, scale, causal, window_left, window_right, dtype, &plan);
 }
 
-extern "C" int fa_fwd_strided(const void* q, const void* k, const void* v, void* o, float* lse,
-                              const long long* strides, int B, int H, int N, int d, float scale, int causal,
-                              int window_left, int window_right, int dtype, void* stream) {
-  FwdPlan plan;
-  const int st =
-      plan_fwd(q, k, v, o, lse, strides, B, H, N, d, scale, causal, window_left, window_right, dtype, &plan);
-  if (st != FA_OK || plan.nblocks == 0) return st;
+namespace {
 
+// Workgroups of the forward kernel that fit on the chip at once (256
+// compute units; two per unit where the kernel runs two waves per SIMD).
+int resident_blocks(int d, int dtype) { return (dtype == FA_F32 || d == 256) ? 256 : 512; }
+
+// Key tiles per part (of the widest query tile) below which a part does
+// not pay for its partial result and the merge: measured on one GPU over
+// low-occupancy shapes (d = 64 .. 256, N = 256 .. 16384). Causal grids
+// split at shorter ranges, because their longest query tile sets the time.
+constexpr int kMinTilesCausal = 16;
+constexpr int kMinTiles = 32;
+
+// Parts for a grid of nblocks workgroups: none while the grid fills half
+// the chip; otherwise enough to fill it, as long as each part of the widest
+// query tile keeps the minimum number of key tiles; at most 16.
+int choose_splits(long long nblocks, int N, int d, int causal, int wl, int wr, int dtype) {
+  const int slots = resident_blocks(d, dtype);
+  if (nblocks * 2 > slots) return 1;
+  long long span = (long long)rows_per_block(dtype) + (wl < 0 ? N : wl) + (causal || wr == 0 ? 0 : (wr < 0 ? N : wr));
+  span = std::min<long long>(span, N);
+  const int tiles = (int)((span + fa::kBc - 1) / fa::kBc);
+  int s = (int)(slots / std::max<long long>(nblocks, 1));
+  s = std::min(s, tiles / (causal ? kMinTilesCausal : kMinTiles));
+  s = std::min(s, 16);
+  return std::max(s, 1);
+}
+
+long long workspace_bytes_for(int B, int H, int N, int d, int nsplit) {
+  if (nsplit <= 1) return 0;
+  return (long long)nsplit * B * H * N * (long long)(d + 1) * (long long)sizeof(float);
+}
+
+// Enqueues the forward kernel (and, with a split, the merge) for a plan
+// that passed plan_fwd.
+int launch_fwd(const FwdPlan& plan, const void* q, const void* k, const void* v, void* o, float* lse, int B,
+               int H, int N, int d, float scale, int causal, int window_left, int window_right, int dtype,
+               float* part, int nsplit, hipStream_t stream) {
   // log2(e) is folded into the scale: exp(x * scale) == exp2(x * c).
   const float c = (float)((double)scale * 1.4426950408889634074);
   int h_arg = H, n_arg = N, nqt_arg = plan.nqt, nb_arg = (int)plan.nblocks;
@@ -152,24 +195,111 @@ extern "C" int fa_fwd_strided(const void* q, const void* k, const void* v, void*
   int wl = window_left < 0 ? kUnbounded : window_left;
   int wr = window_right < 0 ? kUnbounded : window_right;
   if (causal) wr = 0;
-  fa::View* const view = plan.view;
+  fa::View view[4] = {plan.view[0], plan.view[1], plan.view[2], plan.view[3]};
+  fa::SplitOut sp{nsplit > 1 ? part : nullptr, nsplit > 1 ? nsplit : 1, B * H};
   void* args[] = {(void*)&q,       (void*)&k,       (void*)&v,       (void*)&o,     (void*)&lse,
                   (void*)&view[0], (void*)&view[1], (void*)&view[2], (void*)&view[3], (void*)&h_arg,
                   (void*)&n_arg,   (void*)&nqt_arg, (void*)&nb_arg,  (void*)&c_arg, (void*)&wl,
-                  (void*)&wr};
+                  (void*)&wr,      (void*)&sp};
 
   const void* fn = nullptr;
+  const void* merge = nullptr;
   if (dtype == FA_F32) {
     fn = (const void*)pick32(d, causal != 0);
+    merge = pick_merge<float>(d);
   } else if (dtype == FA_BF16) {
     fn = (const void*)pick16<fa::Bf16>(d, causal != 0);
+    merge = pick_merge<fa::Bf16>(d);
   } else {
     fn = (const void*)pick16<fa::F16>(d, causal != 0);
+    merge = pick_merge<fa::F16>(d);
   }
-  if (!fn) return FA_ERR_HEADDIM;
-  const hipError_t e = hipLaunchKernel(fn, dim3((unsigned)plan.nblocks), dim3(fa::kThreads), args, 0,
-                                       (hipStream_t)stream);
-  return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+  if (!fn || !merge) return FA_ERR_HEADDIM;
+  long long rows = (long long)B * H * N;
+  const int rpb = fa::kThreads / (d / 4);  // rows per merge workgroup
+  const long long mblocks = (rows + rpb - 1) / rpb;
+  if (sp.part && mblocks > INT_MAX) return FA_ERR_SHAPE;
+  if (hipLaunchKernel(fn, dim3((unsigned)plan.nblocks, (unsigned)sp.nsplit), dim3(fa::kThreads), args, 0, stream) !=
+      hipSuccess)
+    return FA_ERR_LAUNCH;
+  if (sp.part) {
+    const float* part_c = part;
+    int ns = nsplit;
+    fa::View vo = view[3];
+    void* margs[] = {(void*)&part_c, (void*)&ns, (void*)&o, (void*)&vo, (void*)&lse, (void*)&h_arg, (void*)&n_arg,
+                     (void*)&rows};
+    if (hipLaunchKernel(merge, dim3((unsigned)mblocks), dim3(fa::kThreads), margs, 0, stream) != hipSuccess)
+      return FA_ERR_LAUNCH;
+  }
+  return FA_OK;
+}
+
+}  // namespace
+
+extern "C" int fa_fwd_strided(const void* q, const void* k, const void* v, void* o, float* lse,
+                              const long long* strides, int B, int H, int N, int d, float scale, int causal,
+                              int window_left, int window_right, int dtype, void* stream) {
+  FwdPlan plan;
+  const int st =
+      plan_fwd(q, k, v, o, lse, strides, B, H, N, d, scale, causal, window_left, window_right, dtype, &plan);
+  if (st != FA_OK || plan.nblocks == 0) return st;
+  return launch_fwd(plan, q, k, v, o, lse, B, H, N, d, scale, causal, window_left, window_right, dtype, nullptr, 1,
+                    (hipStream_t)stream);
+}
+
+extern "C" int fa_fwd_num_splits(int B, int H, int N, int d, int causal, int window_left, int window_right,
+                                 int dtype, int* num_splits) {
+  long long nblocks = 0;
+  int nqt = 0;
+  const int st = check_shape(B, H, N, d, causal, dtype, &nblocks, &nqt);
+  if (st != FA_OK) return st;
+  if (window_left < -1 || window_right < -1) return FA_ERR_ARG;
+  if (!num_splits) return FA_ERR_NULL;
+  *num_splits = nblocks == 0 ? 1 : choose_splits(nblocks, N, d, causal, window_left, window_right, dtype);
+  return FA_OK;
+}
+
+extern "C" int fa_fwd_splitkv_workspace(int B, int H, int N, int d, int num_splits, long long* bytes) {
+  if (B < 0 || H < 0 || N < 0 || d < 0) return FA_ERR_SHAPE;
+  if (num_splits < 1 || num_splits > kMaxSplits) return FA_ERR_ARG;
+  if (!bytes) return FA_ERR_NULL;
+  *bytes = workspace_bytes_for(B, H, N, d, num_splits);
+  return FA_OK;
+}
+
+extern "C" int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse,
+                              const long long* strides, void* workspace, long long workspace_bytes, int num_splits,
+                              int B, int H, int N, int d, float scale, int causal, int window_left,
+                              int window_right, int dtype, void* stream) {
+  if (num_splits < 0 || num_splits > kMaxSplits) return FA_ERR_ARG;
+  FwdPlan plan;
+  int st = plan_fwd(q, k, v, o, lse, strides, B, H, N, d, scale, causal, window_left, window_right, dtype, &plan);
+  if (st != FA_OK || plan.nblocks == 0) return st;
+  int ns = num_splits == 0 ? choose_splits(plan.nblocks, N, d, causal, window_left, window_right, dtype)
+                           : num_splits;
+  float* part = nullptr;
+  if (ns > 1) {
+    const long long need = workspace_bytes_for(B, H, N, d, ns);
+    if (!workspace) return FA_ERR_NULL;
+    if ((uintptr_t)workspace & 15) return FA_ERR_ALIGN;
+    if (workspace_bytes < need) return FA_ERR_ARG;
+    // The workspace is written: it may not overlap any operand.
+    const fa::host::Dims g{B, H, N, d, dtype == FA_F32 ? 4 : 2};
+    const void* ptrs[4] = {q, k, v, o};
+    for (int i = 0; i < 4; ++i) {
+      fa::host::Operand op;
+      fa::View unused;
+      st = fa::host::make_operand(ptrs[i], strides ? strides + 3 * i : nullptr, g, &op, &unused);
+      if (st != FA_OK) return st;
+      if (fa::host::ranges_overlap((uintptr_t)workspace, need, op.p, op.span)) return FA_ERR_ARG;
+    }
+    if (fa::host::ranges_overlap((uintptr_t)workspace, need, (uintptr_t)lse,
+                                 (long long)B * H * N * (long long)sizeof(float)))
+      return FA_ERR_ARG;
+    part = (float*)workspace;
+  }
+  return launch_fwd(plan, q, k, v, o, lse, B, H, N, d, scale, causal, window_left, window_right, dtype, part, ns,
+                    (hipStream_t)stream);
 }
 
 extern "C" int fa_fwd_window(const void* q, const void* k, const void* v, void* o, float* lse, int B,

@@ -97,6 +97,29 @@ __device__ __forceinline__ long long view_base(const View& v, int bh, int H) {
   return (long long)b * v.b + (long long)(bh - b * H) * v.h;
 }
 
+// Split-KV partial results. With nsplit > 1 the launch grid has nsplit
+// rows (blockIdx.y = s), and workgroup (x, s) covers the s-th of nsplit
+// contiguous, near-equal parts of its query tile's key tiles: tiles
+// floor(n s / nsplit) .. floor(n (s + 1) / nsplit) - 1 of its n tiles. It
+// writes, for each of its query rows, the attention over those keys alone,
+// normalised (O_s), and its LSE_s, both fp32, into the workspace `part`:
+// O_s at part[((s * BH + bh) * N + i) * d + c], then LSE_s at
+// part[nsplit * BH * N * d + (s * BH + bh) * N + i] (BH = B * H). A row with
+// no visible key in the part gets O_s = 0 and LSE_s = -inf.
+struct SplitOut {
+  float* part;  // NULL: no split, write O and LSE directly
+  int nsplit;
+  int nbh;      // B * H
+};
+
+// The part [t_lo, t_lo + nkt) of a tile range that split s of n covers.
+__device__ __forceinline__ void split_range(int s, int n, int& t_lo, int& nkt) {
+  const int a = (int)((long long)nkt * s / n);
+  const int e = (int)((long long)nkt * (s + 1) / n);
+  t_lo += a;
+  nkt = e - a;
+}
+
 // Floor of a / b for b > 0 and any sign of a.
 __device__ __forceinline__ int floor_div(int a, int b) { return a >= 0 ? a / b : -((b - 1 - a) / b); }
 
@@ -321,7 +344,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
 void fwd16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                   const uint16_t* __restrict__ V, uint16_t* __restrict__ O,
                   float* __restrict__ LSE, View vq, View vk, View vv, View vo, int H, int N, int nqt,
-                  int nblocks, float c, int wl, int wr) {
+                  int nblocks, float c, int wl, int wr, SplitOut sp) {
   using G = Geo16<D>;
   typedef short s16x4 __attribute__((ext_vector_type(4)));
   typedef __attribute__((address_space(3))) s16x4* lds_s16x4_t;
@@ -365,10 +388,25 @@ void fwd16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K
   // i - wl .. i + wr; wr is 0 when causal, and an unbounded side is 2^30).
   // Tiles full_lo .. full_hi are visible to every row of the block.
   const int q_lo = qt * kBr;
-  const int t_lo = max(q_lo - wl, 0) / kBc;
-  const int nkt = min(min(q_lo + kBr - 1, N - 1) + wr, N - 1) / kBc + 1 - t_lo;
+  int t_lo = max(q_lo - wl, 0) / kBc;
+  int nkt = min(min(q_lo + kBr - 1, N - 1) + wr, N - 1) / kBc + 1 - t_lo;
   const int full_lo = (max(q_lo + kBr - 1 - wl, 0) + kBc - 1) / kBc;
   const int full_hi = floor_div(min(N, q_lo + wr + 1) - kBc, kBc);
+  if (sp.part) {
+    split_range(blockIdx.y, sp.nsplit, t_lo, nkt);
+    if (nkt == 0) {  // an empty part: O_s = 0, LSE_s = -inf
+      if (qrow < N) {
+        float* op = sp.part + (((size_t)blockIdx.y * sp.nbh + bh) * N + qrow) * D;
+#pragma unroll
+        for (int t = 0; t < D / 32; ++t)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) *(f32x4*)(op + 32 * t + 8 * g + 4 * hh) = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (hh == 0)
+          sp.part[(size_t)sp.nsplit * sp.nbh * N * D + ((size_t)blockIdx.y * sp.nbh + bh) * N + qrow] = -INFINITY;
+      }
+      return;
+    }
+  }
 
   // Tile-invariant source offsets of this lane's copy slots.
   uint32_t koff[G::kKPW], voff[G::kVPW];
@@ -615,6 +653,23 @@ void fwd16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K
   pv_tile((nkt - 1) & 1 ? v1s : v0s, pfa);
 
   const float l_tot = pair_sum(l_run);
+  if (sp.part) {
+    // A part may hold no visible key of a row (l = 0): O_s = 0, LSE_s = -inf.
+    const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
+    if (qrow < N) {
+      float* op = sp.part + (((size_t)blockIdx.y * sp.nbh + bh) * N + qrow) * D;
+#pragma unroll
+      for (int t = 0; t < D / 32; ++t)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+          *(f32x4*)(op + 32 * t + 8 * g + 4 * hh) = f32x4{acc[t][4 * g] * inv, acc[t][4 * g + 1] * inv,
+                                                          acc[t][4 * g + 2] * inv, acc[t][4 * g + 3] * inv};
+      if (hh == 0)
+        sp.part[(size_t)sp.nsplit * sp.nbh * N * D + ((size_t)blockIdx.y * sp.nbh + bh) * N + qrow] =
+            l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
+    }
+    return;
+  }
   const float inv = 1.0f / l_tot;
   if (qrow < N) {
     uint16_t* orow = O + (long long)qrow * vo.r;
@@ -654,7 +709,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
 void fwd32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
                   const float* __restrict__ V, float* __restrict__ O,
                   float* __restrict__ LSE, View vq, View vk, View vv, View vo, int H, int N, int nqt,
-                  int nblocks, float c, int wl, int wr) {
+                  int nblocks, float c, int wl, int wr, SplitOut sp) {
   constexpr int DCH = D / 4;                  // 16-byte chunks per row
   constexpr int VSTRIDE = D + 8;              // floats per padded V row
   constexpr int KS_BYTES = kBc * D * 4;
@@ -696,8 +751,13 @@ void fwd32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
   // Key tiles the block needs (query i sees keys i - wl .. i + wr; wr is 0
   // when causal, an unbounded side is 2^30).
   const int q_lo = qt * kBr32;
-  const int t_lo = max(q_lo - wl, 0) / kBc;
-  const int t_end = min(min(q_lo + kBr32 - 1, N - 1) + wr, N - 1) / kBc + 1;
+  int t_lo = max(q_lo - wl, 0) / kBc;
+  int t_end = min(min(q_lo + kBr32 - 1, N - 1) + wr, N - 1) / kBc + 1;
+  if (sp.part) {  // an empty part runs no iteration and stores O_s = 0, LSE_s = -inf
+    int nkt = t_end - t_lo;
+    split_range(blockIdx.y, sp.nsplit, t_lo, nkt);
+    t_end = t_lo + nkt;
+  }
 
   f32x4 kreg[PF ? CH : 1], vreg[PF ? CH : 1];
 
@@ -805,6 +865,23 @@ void fwd32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
   }
 
   const float l_tot = wave_pair_sum(l_run);
+  if (sp.part) {
+    // A part may hold no visible key of a row (l = 0): O_s = 0, LSE_s = -inf.
+    const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
+    if (qrow < N) {
+      float* op = sp.part + (((size_t)blockIdx.y * sp.nbh + bh) * N + qrow) * D;
+#pragma unroll
+      for (int t = 0; t < D / 32; ++t)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+          *(f32x4*)(op + 32 * t + 8 * g + 4 * hh) = f32x4{acc[t][4 * g] * inv, acc[t][4 * g + 1] * inv,
+                                                          acc[t][4 * g + 2] * inv, acc[t][4 * g + 3] * inv};
+      if (hh == 0)
+        sp.part[(size_t)sp.nsplit * sp.nbh * N * D + ((size_t)blockIdx.y * sp.nbh + bh) * N + qrow] =
+            l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
+    }
+    return;
+  }
   const float inv = 1.0f / l_tot;
   if (qrow < N) {
     float* orow = O + (long long)qrow * vo.r;
@@ -819,6 +896,48 @@ void fwd32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
     }
     if (hh == 0) LSE[qrow] = (m_run + __log2f(l_tot)) * kLn2;
   }
+}
+
+// ---------------------------------------------------------------------------
+// Split-KV merge: the LSE-weighted combination of the nsplit partial results
+// in `part` (layout of SplitOut):
+//   LSE = ln sum_s exp(LSE_s),  O = sum_s exp(LSE_s - LSE) O_s,
+// with the largest LSE_s as the exponent reference (parts with LSE_s = -inf
+// weigh 0). One row per D/4 consecutive lanes, 16 bytes of each part per
+// lane; O is rounded once to the output type T (Bf16, F16 or float) and
+// stored through its view. Bound by the reads of the parts.
+template <class T, int D>
+__global__ __launch_bounds__(kThreads) void merge_kernel(const float* __restrict__ part, int nsplit,
+                                                         void* __restrict__ O, View vo,
+                                                         float* __restrict__ LSE, int H, int N,
+                                                         long long rows) {
+  constexpr int TPR = D / 4;
+  constexpr int RPB = kThreads / TPR;
+  constexpr float kLog2e = 1.44269504088896340736f;
+  const long long row = (long long)blockIdx.x * RPB + threadIdx.x / TPR;
+  const int c = threadIdx.x % TPR;
+  if (row >= rows) return;
+  const float* const lp = part + (size_t)nsplit * rows * D + row;
+  float m = -INFINITY;
+  for (int s = 0; s < nsplit; ++s) m = fmaxf(m, lp[(size_t)s * rows]);
+  const float m_use = m == -INFINITY ? 0.f : m;
+  float l = 0.f;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int s = 0; s < nsplit; ++s) {
+    const float w = __builtin_amdgcn_exp2f((lp[(size_t)s * rows] - m_use) * kLog2e);
+    l += w;
+    acc += w * *(const f32x4*)(part + ((size_t)s * rows + row) * D + 4 * c);
+  }
+  acc *= l > 0.f ? 1.0f / l : 0.f;
+  const int bh = (int)(row / N);
+  const int i = (int)(row - (long long)bh * N);
+  const long long off = view_base(vo, bh, H) + (long long)i * vo.r + 4 * c;
+  if constexpr (std::is_same<T, float>::value) {
+    *(f32x4*)((float*)O + off) = acc;
+  } else {
+    *(u32x2*)((uint16_t*)O + off) = u32x2{T::pack(acc[0], acc[1]), T::pack(acc[2], acc[3])};
+  }
+  if (c == 0) LSE[row] = l > 0.f ? m_use + __logf(l) : -INFINITY;
 }
 
 }  // namespace fa
