@@ -99,12 +99,13 @@ def cpu_baseline(q, k, v, scale, causal, heads):
     """Times the fp64 oracle (as it stands) on `heads` whole heads."""
     from oracle import attention_ref
 
-    threads = None
+    threads, blas = None, None
     try:
         from threadpoolctl import threadpool_info
 
-        threads = max((p.get("num_threads", 0) for p in threadpool_info() if p.get("user_api") == "blas"),
-                      default=None)
+        pools = [p for p in threadpool_info() if p.get("user_api") == "blas"]
+        threads = max((p.get("num_threads", 0) for p in pools), default=None)
+        blas = ", ".join(sorted({str(p.get("internal_api")) for p in pools})) or None
     except Exception:
         pass
     qs, ks, vs = (t[:, :heads].double().numpy() for t in (q, k, v))
@@ -118,6 +119,9 @@ def cpu_baseline(q, k, v, scale, causal, heads):
         "unit": "TFLOP/s",
         "cores": threads or os.cpu_count(),
         "kind": "oracle",
+        "cpu_count": os.cpu_count(),
+        "affinity": len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else None,
+        "blas": blas,
         "sample": f"{heads} of {q.shape[1]} heads (all {N} query rows each), fp64 numpy, {dt:.1f} s",
     }
 
@@ -162,6 +166,37 @@ def bench_backward(fa, inputs, dev, stream, steps, warmup, no_parity):
             "d": c["D"], "kernel_ms_mean": round(kms, 4), "tflops": round(tf, 2),
             "frac": round(tf / PEAK_BF16_TFLOPS, 4), "flops_counted": "2.5x the forward's metric flops",
             "parity_ok": ok, "max_rel_err_2_heads": err}
+
+
+def bench_backward_d256(fa, inputs, dev, stream, steps, warmup):
+    """fa_bwd on long-causal-d256 (d = 256: dQ, then dV and dK in two
+    passes). The fp64 gradient oracle is too slow at N = 16384; parity at
+    d = 256 is in the GPU tests (2 heads at N = 4096 and the length and
+    window cases). Reported: time and finiteness of every gradient."""
+    import numpy as np
+    import torch
+
+    c = inputs.CONFIGS[PRIMARY]
+    log(f"[bench] backward on config {PRIMARY} ({c['name']}): inputs")
+    q, k, v = inputs.make_config(PRIMARY)
+    g = torch.Generator().manual_seed(44)
+    do = torch.randn(q.shape, generator=g, dtype=torch.float32).to(q.dtype)
+    qd, kd, vd, dod = (t.to(dev) for t in (q, k, v, do))
+    o, lse = fa.fwd(qd, kd, vd, causal=True)
+    dq, dk, dv = (torch.full_like(qd, float("nan")) for _ in range(3))
+    delta = torch.empty(qd.shape[:3], dtype=torch.float32, device=dev)
+
+    def step():
+        fa.bwd(qd, kd, vd, o, lse, dod, causal=True, dq=dq, dk=dk, dv=dv, delta=delta)
+
+    _, per = time_launches(step, stream, steps, warmup)
+    finite = all(bool(torch.isfinite(x).all()) for x in (dq, dk, dv))
+    kms = float(np.mean(per))
+    tf = 2.5 * metric_flops(c) / (kms * 1e-3) / 1e12
+    return {"workload": "long-causal-d256 backward (dQ, dK, dV)", "kernel_ms_mean": round(kms, 4),
+            "tflops": round(tf, 2), "frac": round(tf / PEAK_BF16_TFLOPS, 4),
+            "flops_counted": "2.5x the forward's metric flops", "all_finite": finite,
+            "parity": "tests/test_gpu_bwd.py (d = 256: every length/window case and 2 heads at N = 4096)"}
 
 
 def bench_packed(fa, inputs, dev, stream, steps, warmup):
@@ -267,6 +302,9 @@ def main():
     ap.add_argument("--cpu-heads", type=int, default=10)
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-parity", action="store_true", help="skip the oracle check (profiling runs)")
+    ap.add_argument("--flush", action="store_true",
+                    help="also time the main workload with a 512 MiB buffer written between calls "
+                         "(outside the events): a cold-cache figure")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 1 GiB device-to-device copy 3 times, to scale HBM counters")
     args = ap.parse_args()
@@ -351,6 +389,27 @@ def main():
         "parity": {"max_abs_dO": par["err_o"], "max_abs_dLSE": par["err_l"], "ok": par["ok"],
                    "rows_checked_per_head": int(len(rows))},
     }
+    if args.flush:
+        log("[bench] cold-cache timing: 512 MiB written between calls")
+        scratch = torch.empty(1 << 27, dtype=torch.float32, device=dev)
+        q_d, k_d, v_d = (t.to(dev) for t in (q, k, v))
+        o_d = torch.empty_like(q_d)
+        l_d = torch.empty(q_d.shape[:3], dtype=torch.float32, device=dev)
+        cold = []
+        for i in range(args.warmup + args.steps):
+            scratch.fill_(float(i))
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fa.fwd(q_d, k_d, v_d, softmax_scale=scale, causal=c["causal"], out=o_d, lse=l_d)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            if i >= args.warmup:
+                cold.append(e0.elapsed_time(e1))
+        cold.sort()
+        out["cold_cache"] = {"kernel_ms_median": round(cold[len(cold) // 2], 4),
+                             "kernel_ms_mean": round(float(np.mean(cold)), 4),
+                             "note": "512 MiB scratch written between calls, outside the events"}
+        del scratch, q_d, k_d, v_d, o_d, l_d
     if not args.no_secondary:
         rows4 = np.unique(np.concatenate([np.arange(256), np.arange(2048 - 32, 2048)]))
         c4, _, par4, wall4, per4 = run_config(SECONDARY, max(args.steps, 20), args.warmup, rows4)
@@ -390,6 +449,7 @@ def main():
         # gradient, halved for causal), the usual accounting.
         out["backward"] = bench_backward(fa, inputs, dev, stream, max(args.steps, 10), args.warmup,
                                          args.no_parity)
+        out["backward_d256"] = bench_backward_d256(fa, inputs, dev, stream, 5, 2)
         out["packed"] = bench_packed(fa, inputs, dev, stream, max(args.steps, 20), args.warmup)
         out["splitkv"] = bench_splitkv(fa, inputs, dev, stream, max(args.steps, 20), args.warmup, args.no_parity)
     if args.calibrate_copy:
@@ -407,6 +467,8 @@ def main():
     failed = [par["ok"]] + [out[k]["parity_ok"] for k in ("secondary", "fp32", "window", "backward", "packed",
                                                           "splitkv")
                           if k in out]
+    if "backward_d256" in out:
+        failed.append(out["backward_d256"]["all_finite"])
     if any(f is False for f in failed):
         sys.exit(1)
 

@@ -211,15 +211,15 @@ int fa_fwd_splitkv_workspace(int B, int H, int N, int d, int num_splits, long lo
  * delta       device pointer, [B, H, N] float32; written with delta_i (it is
  *             both a result and the scratch the kernels share).
  * B, H, N, scale, causal, window_left, window_right, stream: as fa_fwd_window.
- * d           64 or 128.
+ * d           64, 128 or 256.
  * dtype       FA_F16 or FA_BF16 (fp32 is not supported by the backward).
  *
  * Ownership, synchronisation and errors as fa_fwd: the caller owns every
  * buffer, nothing is allocated, and three kernels are enqueued on stream in
  * order (delta, then dq, then dk/dv); the result does not depend on
  * scheduling (no atomics). The outputs dq, dk, dv, delta must not overlap
- * each other or any input (FA_ERR_ARG). FA_ERR_HEADDIM for d other than 64
- * or 128, FA_ERR_DTYPE for fp32 or an unknown dtype; all pointers 16-byte
+ * each other or any input (FA_ERR_ARG). FA_ERR_HEADDIM for d other than 64,
+ * 128 or 256, FA_ERR_DTYPE for fp32 or an unknown dtype; all pointers 16-byte
  * aligned except lse and delta (4-byte).
  */
 int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,

@@ -105,7 +105,7 @@ def call_bwd(**kw):
 
 @pytest.mark.parametrize("kw,code", [
     (dict(B=-1), -2), (dict(N=1 << 30), -2),
-    (dict(d=256), -3), (dict(d=32), -3),
+    (dict(d=512), -3), (dict(d=32), -3),
     (dict(dtype=2), -4), (dict(dtype=7), -4),
     (dict(causal=3), -6), (dict(scale=float("nan")), -6), (dict(wl=-2), -6),
     (dict(q=0), -1), (dict(do=0), -1), (dict(delta=0), -1), (dict(dv=0), -1),

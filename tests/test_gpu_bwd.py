@@ -76,7 +76,7 @@ def check(grads, q, k, v, do, scale, causal, window, dtype):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
-@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("D", [64, 128, 256])
 @pytest.mark.parametrize("causal", [False, True])
 def test_bwd_lengths(dtype, D, causal):
     """Single and partial tiles, exact multiples of the 64-row and 128-row
@@ -89,7 +89,7 @@ def test_bwd_lengths(dtype, D, causal):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
-@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("D", [64, 128, 256])
 def test_bwd_windows(dtype, D):
     for causal, window, N in ((False, (0, 0), 200), (False, (5, 3), 300), (True, (64, 0), 300),
                               (False, (130, -1), 400), (False, (-1, 70), 400), (True, (1000, 1000), 150)):
@@ -111,6 +111,15 @@ def test_bwd_batch_heads_long_causal():
     causal): many key blocks and query tiles per head."""
     q, k, v, do = make(1, 4, 2048, 128, "bf16", seed=42)
     scale = 1.0 / math.sqrt(128)
+    grads, _, _ = run_bwd(q, k, v, do, scale, True)
+    check(grads, q, k, v, do, scale, True, (-1, -1), "bf16")
+
+
+def test_bwd_d256_long_causal():
+    """d = 256 (two dK/dV passes): a slice of the long-causal-d256 shape,
+    2 heads at N = 4096."""
+    q, k, v, do = make(1, 2, 4096, 256, "bf16", seed=43)
+    scale = 1.0 / 16
     grads, _, _ = run_bwd(q, k, v, do, scale, True)
     check(grads, q, k, v, do, scale, True, (-1, -1), "bf16")
 
@@ -155,6 +164,6 @@ def test_bwd_python_errors():
     lse = torch.zeros(1, 1, 8, device="cuda")
     with pytest.raises(NotImplementedError):
         fa.bwd(x, x, x, x, lse, x)
-    y = torch.zeros(1, 1, 8, 256, dtype=torch.bfloat16, device="cuda")
+    y = torch.zeros(1, 1, 8, 96, dtype=torch.bfloat16, device="cuda")
     with pytest.raises(NotImplementedError):
         fa.bwd(y, y, y, y, lse, y)

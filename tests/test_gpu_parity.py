@@ -182,6 +182,23 @@ def test_single_key_and_causal_first_row(dtype):
     assert torch.equal(o[:, :, 0], v[:, :, 0])
 
 
+@pytest.mark.parametrize("dtype,D", [("bf16", 256), ("f16", 128), ("f32", 64)])
+def test_causal_rows_ignore_later_keys(dtype, D):
+    """Causal structure: changing the keys and values after row i0 leaves
+    rows 0..i0 (O and LSE) bitwise unchanged; later rows do change."""
+    N, i0 = 700, 300
+    q, k, v = inputs.make_qkv(1, 2, N, D, dtype, seed=14)
+    o1, l1 = run(q, k, v, 0.1, True)
+    k2, v2 = k.clone(), v.clone()
+    g = torch.Generator().manual_seed(15)
+    k2[:, :, i0 + 1:] = torch.randn(k2[:, :, i0 + 1:].shape, generator=g).to(k.dtype) * 3
+    v2[:, :, i0 + 1:] = torch.randn(v2[:, :, i0 + 1:].shape, generator=g).to(v.dtype) * 3
+    o2, l2 = run(q, k2, v2, 0.1, True)
+    assert torch.equal(o1[:, :, :i0 + 1], o2[:, :, :i0 + 1])
+    assert torch.equal(l1[:, :, :i0 + 1], l2[:, :, :i0 + 1])
+    assert not torch.equal(o1[:, :, i0 + 1:], o2[:, :, i0 + 1:])
+
+
 def test_constant_values():
     q, k, _ = inputs.make_qkv(1, 4, 777, 256, "bf16", seed=12)
     v = torch.full_like(q, 1.5)

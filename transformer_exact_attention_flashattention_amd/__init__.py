@@ -28,7 +28,7 @@ flash-attn 2.8.3 build guide, intelliparadigm.com, calls):
   differentiable.
 * ``bwd(q, k, v, o, lse, do, softmax_scale=None, causal=False,
   window_size=(-1, -1)) -> (dq, dk, dv)``: the backward pass (fp16/bf16,
-  d = 64 or 128), recomputing the attention weights from q, k and the
+  d = 64, 128 or 256), recomputing the attention weights from q, k and the
   forward's lse (section 9.2 item 2 of the build guide); strided views as
   for ``fwd``, including the gradients passed in as dq, dk, dv.
 * ``attention(q, k, v, softmax_scale=None, causal=False,
@@ -361,8 +361,8 @@ def bwd(q, k, v, o, lse, do, softmax_scale=None, causal=False, window_size=(-1, 
     if code == FA_F32:
         raise NotImplementedError("the backward pass supports float16 and bfloat16")
     B, H, N, d = q.shape
-    if d not in (64, 128):
-        raise NotImplementedError(f"head dimension {d} is not supported by the backward pass (64, 128)")
+    if d not in (64, 128, 256):
+        raise NotImplementedError(f"head dimension {d} is not supported (64, 128, 256)")
     _check_rowstat("lse", lse, B, H, N, q.device)
     scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
     new = lambda: torch.empty((B, H, N, d), dtype=q.dtype, device=q.device)  # noqa: E731

@@ -1,5 +1,5 @@
 // fa_bwd.hip - backward pass of exact attention (fp16 / bf16 inputs, head
-// dimension 64 or 128): argument checks, kernels and launches of fa_bwd.
+// dimension 64, 128 or 256): argument checks, kernels and launches of fa_bwd.
 //
 // The forward keeps only O and the row statistic LSE; the backward
 // recomputes the attention weights from Q, K and LSE instead of storing the
@@ -79,17 +79,22 @@ typedef __attribute__((address_space(3))) s16x4* lds_s16x4_t;
 
 // A lane's LDS byte offsets for its operand reads, with the chunk swizzle
 // resolved once (swz depends on r & 15 only, so moving by 16 rows adds a
-// plain row offset that the reads take as an immediate).
+// plain row offset that the reads take as an immediate). The swizzle flips
+// only the low 4 bits of a chunk index, so chunks 16 and up sit exactly 256
+// bytes after chunks 0 .. 15 of the same row: only the offsets of the first
+// 16 chunks are kept, and the rest is an immediate.
 template <int D>
 struct Operands {
-  int ro[D / 16];  // A operand of X B, k-step s: row sigma(n), chunk 2s + hh
-  int tl[D / 32];  // A operand of X^T B, 32-column block tb: low 8 bytes
-  int th[D / 32];  //   and high 8 bytes (rows 4 further), for 16-row step 0
+  static constexpr int kRo = D / 16 < 8 ? D / 16 : 8;
+  static constexpr int kTr = D / 32 < 4 ? D / 32 : 4;
+  int ro[kRo];  // A operand of X B, k-step s: row sigma(n), chunk 2s + hh
+  int tl[kTr];  // A operand of X^T B, 32-column block tb: low 8 bytes
+  int th[kTr];  //   and high 8 bytes (rows 4 further), for 16-row step 0
 
   __device__ __forceinline__ explicit Operands(int lane) {
     const int n = lane & 31, hh = lane >> 5;
 #pragma unroll
-    for (int s = 0; s < D / 16; ++s) ro[s] = at<D>(sigma(n), 2 * s + hh);
+    for (int s = 0; s < kRo; ++s) ro[s] = at<D>(sigma(n), 2 * s + hh);
     // Transposed reads (the lane pattern of the forward kernel's V^T
     // operand): 16-lane block vb, lane vj reads rows r0 and r0 + 4, chunk
     // 4tb + c0, half vj & 1.
@@ -98,7 +103,7 @@ struct Operands {
     const int c0 = 2 * (vb & 1) + ((vj & 3) >> 1);
     const int h8 = 8 * (vj & 1);
 #pragma unroll
-    for (int tb = 0; tb < D / 32; ++tb) {
+    for (int tb = 0; tb < kTr; ++tb) {
       tl[tb] = at<D>(r0, 4 * tb + c0) + h8;
       th[tb] = at<D>(r0 + 4, 4 * tb + c0) + h8;
     }
@@ -106,43 +111,60 @@ struct Operands {
 
   // X B operand: rows rbase + sigma(m) (rbase a multiple of 16).
   __device__ __forceinline__ u32x4 row(const unsigned char* tile, int rbase, int s) const {
-    return *(const u32x4*)(tile + rbase * Tile<D>::kRS + ro[s]);
+    return *(const u32x4*)(tile + rbase * Tile<D>::kRS + 256 * (s / kRo) + ro[s % kRo]);
   }
   // X^T B operand: 16-row k-step ks (rows 16ks ..), 32-column block tb.
   __device__ __forceinline__ u32x4 tr(const unsigned char* tile, int ks, int tb) const {
-    const unsigned char* t = tile + 16 * ks * Tile<D>::kRS;
-    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t)as_lds(t + tl[tb]));
-    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t)as_lds(t + th[tb]));
+    const unsigned char* t = tile + 16 * ks * Tile<D>::kRS + 256 * (tb / kTr);
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t)as_lds(t + tl[tb % kTr]));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t)as_lds(t + th[tb % kTr]));
     const u32x2 l2 = __builtin_bit_cast(u32x2, lo);
     const u32x2 h2 = __builtin_bit_cast(u32x2, hi);
     return u32x4{l2.x, l2.y, h2.x, h2.y};
   }
 };
 
-// Copies of a 64-row tile into an LDS tile of the swizzled layout by
+// Copies of an R-row tile into an LDS tile of the swizzled layout by
 // buffer loads that write LDS directly (no registers): each wave
-// instruction fills 1 KiB, i.e. 4 LDS rows, 16 bytes per lane in lane
-// order; lane l of copy block b writes row 4b + l/16 at physical chunk l%16
-// and so fetches the logical chunk (l%16) ^ swz(row) of that row (for
-// d = 64 the second half of each 256-byte row is padding, filled with a
-// duplicate chunk). Wave w issues blocks w, w + 4, ...; they all share the
-// lane's row modulo 16, hence one source offset plus 16 rows per block.
+// instruction fills 1 KiB, i.e. 1024 / kRS LDS rows, 16 bytes per lane in
+// lane order; lane l of copy block b writes row (1024 / kRS) b + l / L at
+// physical chunk l % L (L = kRS / 16 lanes per row) and so fetches the
+// logical chunk (l % L) ^ swz(row) of that row (for d = 64 the second half
+// of each 256-byte row is padding, filled with a duplicate chunk). Wave w
+// issues blocks w, w + 4, ...: 16 rows apart for 256-byte rows, which all
+// share the lane's row modulo 16 and so one source offset plus 16 rows per
+// block; 8 rows apart for 512-byte rows (d = 256), whose blocks alternate
+// between two swizzles and so two source offsets.
 // Global rows are rs >= 2D bytes apart (the row stride of the operand's
 // view); rows past the end of the sequence are outside the buffer's range.
 template <int D, int R>
 struct TileDma {
-  static constexpr int kBlocks = R * Tile<D>::kRS / 1024;
+  static constexpr int kRS = Tile<D>::kRS;
+  static constexpr int kLPR = kRS / 16;    // lanes per LDS row
+  static constexpr int kRPB = 1024 / kRS;  // LDS rows per copy block
+  static constexpr int kStep = 4 * kRPB;   // rows between a wave's consecutive blocks
+  static constexpr int kNOff = 16 / kStep;  // distinct swizzles among them
+  static constexpr int kBlocks = R * kRS / 1024;
   static constexpr int kPW = kBlocks / 4;  // copy instructions per wave
-  static_assert(kBlocks % 4 == 0, "blocks per wave");
+  static_assert(kBlocks % 4 == 0 && kPW % kNOff == 0, "blocks per wave");
 
-  __device__ static uint32_t lane_offset(int wave, int lane, int rs) {
-    const int row = 4 * wave + (lane >> 4);
-    int c = (lane & 15) ^ swz(row);
-    if (c >= D / 8) c &= D / 8 - 1;  // padding slot
-    return (uint32_t)row * (uint32_t)rs + (uint32_t)(16 * c);
+  struct Off {
+    uint32_t v[kNOff];
+  };
+
+  __device__ static Off lane_offset(int wave, int lane, int rs) {
+    Off o;
+#pragma unroll
+    for (int j = 0; j < kNOff; ++j) {
+      const int row = kRPB * wave + lane / kLPR + kStep * j;
+      int c = (lane % kLPR) ^ swz(row);
+      if (c >= D / 8) c &= D / 8 - 1;  // padding slot
+      o.v[j] = (uint32_t)row * (uint32_t)rs + (uint32_t)(16 * c);
+    }
+    return o;
   }
 
-  __device__ static void issue(const uint16_t* src, int nvalid, int rs, unsigned char* lds, uint32_t off,
+  __device__ static void issue(const uint16_t* src, int nvalid, int rs, unsigned char* lds, const Off& off,
                                int wave) {
 #if defined(__HIP_DEVICE_COMPILE__)
     const int rows = nvalid < R ? (nvalid > 0 ? nvalid : 0) : R;
@@ -151,14 +173,16 @@ struct TileDma {
 #pragma unroll
     for (int i = 0; i < kPW; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, as_lds(lds + 1024 * (wave + 4 * i)), 16,
-                                               off + (uint32_t)(i * 16) * (uint32_t)rs, 0, 0, 0);
+                                               off.v[i % kNOff] + (uint32_t)((i / kNOff) * 16) * (uint32_t)rs,
+                                               0, 0, 0);
 #endif
   }
 };
 
-// One row statistic per query of a 64-query step (LSE or delta) into LDS by
-// a 4-byte copy per lane; every wave copies the same 256 bytes, so that all
-// waves issue the same number of copies.
+// Row statistics (LSE or delta) of the 64 queries from src into LDS by a
+// 4-byte copy per lane; every wave copies the same 256 bytes, so that all
+// waves issue the same number of copies. (With 32-query steps the upper
+// half is the next step's and is not read.)
 __device__ __forceinline__ void dma_row_stat(const float* src, int nvalid, float* lds, int lane) {
 #if defined(__HIP_DEVICE_COMPILE__)
   const int rows = nvalid < 64 ? (nvalid > 0 ? nvalid : 0) : 64;
@@ -205,7 +229,8 @@ __global__ __launch_bounds__(kThreads) void delta_kernel(const uint16_t* __restr
 // when causal; an unbounded side is 2^30).
 // Two waves per SIMD (two workgroups per compute unit), within 256 registers.
 template <class T, int D, bool CAUSAL>
-__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(2, 2)))
+__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
+                          amdgpu_waves_per_eu(D >= 256 ? 1 : 2, D >= 256 ? 1 : 2)))
 void dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
                const float* __restrict__ LSE, const float* __restrict__ Dl, uint16_t* __restrict__ dQ,
@@ -257,8 +282,8 @@ void dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   for (int t = 0; t < D / 32; ++t) acc[t] = f32x16{};
 
   using Dma = TileDma<D, kBc>;
-  const uint32_t koff = Dma::lane_offset(wave, lane, ksb);
-  const uint32_t voff = Dma::lane_offset(wave, lane, vsb);
+  const typename Dma::Off koff = Dma::lane_offset(wave, lane, ksb);
+  const typename Dma::Off voff = Dma::lane_offset(wave, lane, vsb);
   // Rows past N of a ragged last tile keep what the stage held; they are
   // masked, and starting from zeros keeps them finite.
   if (N % kBc != 0) {
@@ -352,14 +377,24 @@ void dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   }
 }
 
-constexpr int kQT = 64;  // query rows per step of the dK/dV kernel
+// Query rows per step of the dK/dV kernel: 64, or 32 at d = 256 so that
+// three stages fit in LDS.
+template <int D>
+constexpr int dkdv_step_rows() {
+  return D >= 256 ? 32 : 64;
+}
+constexpr int kStatSlots = 64;  // LDS floats reserved for LSE (and for delta) per stage
 
 // dK and dV for one 128-key block; wave w owns keys 32w .. 32w+31 of it.
 // One wave per SIMD: K^T, V^T and the dK^T, dV^T accumulators alone take
 // 192 registers per lane at d = 128. Query tiles (Q, dO, LSE, delta) stream
 // through a ring of three LDS stages filled by direct copies issued two
 // steps ahead.
-template <class T, int D, bool CAUSAL>
+// PART selects the gradients: 0 both, 1 dV only, 2 dK only. At d = 256 the
+// two accumulators and the K^T, V^T operands do not fit the registers
+// together, so the host runs the kernel twice (1, then 2), each pass
+// recomputing S (and the dK pass dP) for its own gradient.
+template <class T, int D, bool CAUSAL, int PART>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(1, 1)))
 void dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                  const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
@@ -369,8 +404,10 @@ void dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   // One array per stage: Q tile, dO tile, LSE (natural log), delta. (Few
   // distinct arrays, so that the compiler can still tell the copies into
   // one stage from the reads of another and does not wait on them.)
+  constexpr bool kV = PART != 2, kK = PART != 1;
+  constexpr int kQT = dkdv_step_rows<D>();
   constexpr int TB = kQT * Tile<D>::kRS;
-  constexpr int SB = 2 * TB + 2 * kQT * 4;
+  constexpr int SB = 2 * TB + 2 * kStatSlots * 4;
   __shared__ __attribute__((aligned(1024))) unsigned char st0[SB];
   __shared__ __attribute__((aligned(1024))) unsigned char st1[SB];
   __shared__ __attribute__((aligned(1024))) unsigned char st2[SB];
@@ -398,8 +435,8 @@ void dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   const int krow = key0 + n;
   const Operands<D> op(lane);
   using Dma = TileDma<D, kQT>;
-  const uint32_t qoff = Dma::lane_offset(wave, lane, qsb);
-  const uint32_t goff = Dma::lane_offset(wave, lane, gsb);
+  const typename Dma::Off qoff = Dma::lane_offset(wave, lane, qsb);
+  const typename Dma::Off goff = Dma::lane_offset(wave, lane, gsb);
 
   // K^T and V^T as B operands: lane (n, hh), k-step s holds row krow,
   // columns 16s + 8hh .. +7.
@@ -407,7 +444,8 @@ void dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
 #pragma unroll
   for (int s = 0; s < D / 16; ++s) {
     kf[s] = krow < N ? *(const u32x4*)(K + (long long)krow * vk.r + 16 * s + 8 * hh) : u32x4{0, 0, 0, 0};
-    vf[s] = krow < N ? *(const u32x4*)(V + (long long)krow * vv.r + 16 * s + 8 * hh) : u32x4{0, 0, 0, 0};
+    if constexpr (kK)
+      vf[s] = krow < N ? *(const u32x4*)(V + (long long)krow * vv.r + 16 * s + 8 * hh) : u32x4{0, 0, 0, 0};
   }
 
   // Queries that see a key of the block: i - wl <= j <= i + wr.
@@ -437,14 +475,14 @@ void dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     Dma::issue(Q + (long long)qbase * vq.r, N - qbase, qsb, st, qoff, wave);
     Dma::issue(dO + (long long)qbase * vdo.r, N - qbase, gsb, st + TB, goff, wave);
     dma_row_stat(LSE + qbase, N - qbase, (float*)(st + 2 * TB), lane);
-    dma_row_stat(Dl + qbase, N - qbase, (float*)(st + 2 * TB) + kQT, lane);
+    dma_row_stat(Dl + qbase, N - qbase, (float*)(st + 2 * TB) + kStatSlots, lane);
   };
 
   auto step = [&](int qt, const unsigned char* st, unsigned char* st_next) {
     const unsigned char* const qs = st;
     const unsigned char* const gs = st + TB;
     const float* const ls = (const float*)(st + 2 * TB);
-    const float* const dls = ls + kQT;
+    const float* const dls = ls + kStatSlots;
     // This step's copies landed (those of the next step may still fly),
     // then every wave's copies are visible.
     if (qt + 1 <= qt_hi) wait_vmcnt<kCopies>();
@@ -468,7 +506,7 @@ void dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
 #pragma unroll
       for (int s = 0; s < D / 16; ++s) {
         sa = T::mfma(op.row(qs, 32 * qh, s), kf[s], sa);
-        ga = T::mfma(op.row(gs, 32 * qh, s), vf[s], ga);
+        if constexpr (kK) ga = T::mfma(op.row(gs, 32 * qh, s), vf[s], ga);
       }
       __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 8, 0);
 #pragma unroll
@@ -511,10 +549,10 @@ void dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
             const int r = 8 * cc + 2 * w + e;
             const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sa[r], c, -l2[r]));
             pv[e] = p;
-            dsv[e] = p * (ga[r] - dl[r]);
+            if constexpr (kK) dsv[e] = p * (ga[r] - dl[r]);
           }
-          pp[cc][w] = T::pack(pv[0], pv[1]);
-          dsp[cc][w] = T::pack(dsv[0], dsv[1]);
+          if constexpr (kV) pp[cc][w] = T::pack(pv[0], pv[1]);
+          if constexpr (kK) dsp[cc][w] = T::pack(dsv[0], dsv[1]);
         }
       };
       make_chunk(0);
@@ -524,8 +562,8 @@ void dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
       // k-step's MFMAs.
 #pragma unroll
       for (int tb = 0; tb < D / 32; ++tb) {
-        dv[tb] = T::mfma(op.tr(gs, 2 * qh, tb), pp[0], dv[tb]);
-        dk[tb] = T::mfma(op.tr(qs, 2 * qh, tb), dsp[0], dk[tb]);
+        if constexpr (kV) dv[tb] = T::mfma(op.tr(gs, 2 * qh, tb), pp[0], dv[tb]);
+        if constexpr (kK) dk[tb] = T::mfma(op.tr(qs, 2 * qh, tb), dsp[0], dk[tb]);
       }
       make_chunk(1);
       __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 8, 0);
@@ -538,8 +576,8 @@ void dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int tb = 0; tb < D / 32; ++tb) {
-        dv[tb] = T::mfma(op.tr(gs, 2 * qh + 1, tb), pp[1], dv[tb]);
-        dk[tb] = T::mfma(op.tr(qs, 2 * qh + 1, tb), dsp[1], dk[tb]);
+        if constexpr (kV) dv[tb] = T::mfma(op.tr(gs, 2 * qh + 1, tb), pp[1], dv[tb]);
+        if constexpr (kK) dk[tb] = T::mfma(op.tr(qs, 2 * qh + 1, tb), dsp[1], dk[tb]);
       }
       __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 8, 0);
 #pragma unroll
@@ -571,13 +609,18 @@ void dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     for (int tb = 0; tb < D / 32; ++tb) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        u32x2 ok, ov;
-        ok.x = T::pack(dk[tb][4 * g] * scale, dk[tb][4 * g + 1] * scale);
-        ok.y = T::pack(dk[tb][4 * g + 2] * scale, dk[tb][4 * g + 3] * scale);
-        ov.x = T::pack(dv[tb][4 * g], dv[tb][4 * g + 1]);
-        ov.y = T::pack(dv[tb][4 * g + 2], dv[tb][4 * g + 3]);
-        *(u32x2*)(krow_k + 32 * tb + 8 * g + 4 * hh) = ok;
-        *(u32x2*)(krow_v + 32 * tb + 8 * g + 4 * hh) = ov;
+        if constexpr (kK) {
+          u32x2 ok;
+          ok.x = T::pack(dk[tb][4 * g] * scale, dk[tb][4 * g + 1] * scale);
+          ok.y = T::pack(dk[tb][4 * g + 2] * scale, dk[tb][4 * g + 3] * scale);
+          *(u32x2*)(krow_k + 32 * tb + 8 * g + 4 * hh) = ok;
+        }
+        if constexpr (kV) {
+          u32x2 ov;
+          ov.x = T::pack(dv[tb][4 * g], dv[tb][4 * g + 1]);
+          ov.y = T::pack(dv[tb][4 * g + 2], dv[tb][4 * g + 3]);
+          *(u32x2*)(krow_v + 32 * tb + 8 * g + 4 * hh) = ov;
+        }
       }
     }
   }
@@ -592,21 +635,27 @@ template <class T>
 struct BwdKernels {
   const void* delta;
   const void* dq;
-  const void* dkdv;
+  const void* dkdv;   // both gradients, or dV only when dk_only is set
+  const void* dk_only;
   int rows_per_delta_block;
 };
 
 template <class T, int D>
 BwdKernels<T> pick_d(bool causal) {
+  // d = 256: dV and dK in two passes; otherwise one kernel for both.
+  constexpr int P0 = D >= 256 ? 1 : 0;
+  const void* dk2 = nullptr;
+  if constexpr (D >= 256)
+    dk2 = causal ? (const void*)fa::bwd::dkdv_kernel<T, D, true, 2> : (const void*)fa::bwd::dkdv_kernel<T, D, false, 2>;
   return {(const void*)fa::bwd::delta_kernel<T, D>,
           causal ? (const void*)fa::bwd::dq_kernel<T, D, true> : (const void*)fa::bwd::dq_kernel<T, D, false>,
-          causal ? (const void*)fa::bwd::dkdv_kernel<T, D, true> : (const void*)fa::bwd::dkdv_kernel<T, D, false>,
-          fa::kThreads / (D / 8)};
+          causal ? (const void*)fa::bwd::dkdv_kernel<T, D, true, P0> : (const void*)fa::bwd::dkdv_kernel<T, D, false, P0>,
+          dk2, fa::kThreads / (D / 8)};
 }
 
 template <class T>
 BwdKernels<T> pick(int d, bool causal) {
-  return d == 64 ? pick_d<T, 64>(causal) : pick_d<T, 128>(causal);
+  return d == 64 ? pick_d<T, 64>(causal) : d == 128 ? pick_d<T, 128>(causal) : pick_d<T, 256>(causal);
 }
 
 }  // namespace
@@ -625,7 +674,7 @@ int plan_bwd(const void* q, const void* k, const void* v, const void* o, const f
              float scale, int causal, int window_left, int window_right, int dtype, BwdPlan* plan) {
   if (B < 0 || H < 0 || N < 0 || d < 0) return FA_ERR_SHAPE;
   if (dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_DTYPE;
-  if (d != 64 && d != 128) return FA_ERR_HEADDIM;
+  if (d != 64 && d != 128 && d != 256) return FA_ERR_HEADDIM;
   if (causal != 0 && causal != 1) return FA_ERR_ARG;
   if (!std::isfinite(scale)) return FA_ERR_ARG;
   if (window_left < -1 || window_right < -1) return FA_ERR_ARG;
@@ -633,7 +682,7 @@ int plan_bwd(const void* q, const void* k, const void* v, const void* o, const f
   const long long tiles = (N + fa::kBr - 1) / fa::kBr;
   const long long blocks = (long long)B * (long long)H * tiles;
   if (blocks > INT_MAX) return FA_ERR_SHAPE;
-  if ((long long)B * H * N > (long long)INT_MAX * (fa::kThreads / 16)) return FA_ERR_SHAPE;  // delta grid
+  if ((long long)B * H * N > (long long)INT_MAX * (fa::kThreads / 32)) return FA_ERR_SHAPE;  // delta grid
   plan->tiles = tiles;
   plan->blocks = blocks;
   if (blocks == 0) return FA_OK;
@@ -690,13 +739,14 @@ extern "C" int fa_bwd_strided(const void* q, const void* k, const void* v, const
   const void* kd;
   const void* kq;
   const void* kkv;
+  const void* kk2;
   int rpb;
   if (dtype == FA_BF16) {
     const auto kk = pick<fa::Bf16>(d, causal != 0);
-    kd = kk.delta, kq = kk.dq, kkv = kk.dkdv, rpb = kk.rows_per_delta_block;
+    kd = kk.delta, kq = kk.dq, kkv = kk.dkdv, kk2 = kk.dk_only, rpb = kk.rows_per_delta_block;
   } else {
     const auto kk = pick<fa::F16>(d, causal != 0);
-    kd = kk.delta, kq = kk.dq, kkv = kk.dkdv, rpb = kk.rows_per_delta_block;
+    kd = kk.delta, kq = kk.dq, kkv = kk.dkdv, kk2 = kk.dk_only, rpb = kk.rows_per_delta_block;
   }
   hipStream_t st = (hipStream_t)stream;
 
@@ -730,6 +780,8 @@ extern "C" int fa_bwd_strided(const void* q, const void* k, const void* v, const
                    (void*)&n_arg,   (void*)&nt,      (void*)&nb,      (void*)&c,       (void*)&sc,
                    (void*)&wl,      (void*)&wr};
   if (hipLaunchKernel(kkv, dim3((unsigned)blocks), dim3(fa::kThreads), kargs, 0, st) != hipSuccess)
+    return FA_ERR_LAUNCH;
+  if (kk2 && hipLaunchKernel(kk2, dim3((unsigned)blocks), dim3(fa::kThreads), kargs, 0, st) != hipSuccess)
     return FA_ERR_LAUNCH;
   return FA_OK;
 }
