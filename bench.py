@@ -293,6 +293,54 @@ def bench_splitkv(fa, inputs, dev, stream, steps, warmup, no_parity):
             "max_abs_dLSE": err_l}
 
 
+def bench_graph(fa, inputs, dev, stream):
+    """The two launch-bound workloads (single-head, packed-qkv) called one
+    at a time from Python, and the same calls captured in a HIP graph
+    (20 calls per graph) and replayed: microseconds per call."""
+    import torch
+
+    out = {}
+    for cfg in (1, 2):
+        c = inputs.CONFIGS[cfg]
+        if c["packed"]:
+            qkv = inputs.make_packed_qkv(c["B"], c["N"], c["H"], c["D"], c["dtype"]).to(dev)
+            q, k, v = (qkv[:, :, i].transpose(1, 2) for i in range(3))
+        else:
+            q, k, v = (t.to(dev) for t in inputs.make_config(cfg))
+        B, H, N, D = q.shape
+        o = torch.empty((B, H, N, D), dtype=q.dtype, device=dev)
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+
+        def call():
+            fa.fwd(q, k, v, causal=c["causal"], out=o, lse=lse)
+
+        for _ in range(10):
+            call()
+        torch.cuda.synchronize()
+        n = 200
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(n):
+            call()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        eager_us = e0.elapsed_time(e1) * 1e3 / n
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(20):
+                call()
+        g.replay()
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(n // 20):
+            g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        graph_us = e0.elapsed_time(e1) * 1e3 / n
+        out[c["name"]] = {"eager_us_per_call": round(eager_us, 2), "graph_us_per_call": round(graph_us, 2)}
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -451,6 +499,7 @@ def main():
                                          args.no_parity)
         out["backward_d256"] = bench_backward_d256(fa, inputs, dev, stream, 5, 2)
         out["packed"] = bench_packed(fa, inputs, dev, stream, max(args.steps, 20), args.warmup)
+        out["graph"] = bench_graph(fa, inputs, dev, stream)
         out["splitkv"] = bench_splitkv(fa, inputs, dev, stream, max(args.steps, 20), args.warmup, args.no_parity)
     if args.calibrate_copy:
         log("[bench] copy calibration: 3 x 1 GiB device-to-device copy")
