@@ -1,5 +1,7 @@
 /*
- * fa.h - C ABI of the exact-attention forward library (libfa.so), gfx950.
+ * fa.h - C ABI of the exact-attention library (libfa.so), gfx950: the
+ * forward pass (plain, local window, strided views, split-KV) and the
+ * backward pass, plus host-only queries.
  *
  * The operation is exact softmax attention computed tile by tile with the
  * online-softmax recurrence, so the N x N score matrix is never written to
