@@ -22,6 +22,12 @@ Readings of the pages used here (where they are silent or disagree):
   -1 leaves that side unbounded, so (-1, -1) is full attention. It combines
   with causal by intersection. The diagonal key is always allowed, so no row
   is empty.
+* Fewer queries than keys (Nq < Nk: new tokens against a key/value cache,
+  the inference use of [P1] 11.2, which the pages do not define): the Nq
+  queries are the last Nq positions of the Nk-long sequence, so query row i
+  sits at position i + Nk - Nq and the causal and window tests above apply
+  to that position. With Nq = Nk this is the definition above. A row with no
+  allowed key (possible only with Nq > Nk) gets O = 0 and LSE = -inf.
 """
 
 from __future__ import annotations
@@ -41,6 +47,12 @@ def _check(q, k, v):
         raise ValueError(f"q, k, v must share one [B,H,N,d] shape: {q.shape} {k.shape} {v.shape}")
 
 
+def _check_kv(q, k, v):
+    """q [B, H, Nq, d]; k, v [B, H, Nk, d] (Nk may differ from Nq)."""
+    if q.ndim != 4 or k.shape != v.shape or k.ndim != 4 or k.shape[:2] != q.shape[:2] or k.shape[3] != q.shape[3]:
+        raise ValueError(f"q must be [B,H,Nq,d] and k, v [B,H,Nk,d]: {q.shape} {k.shape} {v.shape}")
+
+
 def _check_window(window):
     left, right = (int(w) for w in window)
     if left < -1 or right < -1:
@@ -48,15 +60,17 @@ def _check_window(window):
     return left, right
 
 
-def allowed_ref(rows, keys, causal, window=(-1, -1)):
+def allowed_ref(rows, keys, causal, window=(-1, -1), offset=0):
     """Boolean [len(rows), len(keys)]: may query row i attend to key j?
 
-    causal: j <= i ([P3] 1.1 lower-triangular mask). window (left, right):
-    j >= i - left and j <= i + right, each side only when >= 0 (the reading
-    of [P1] 10.1 ``window_size`` stated in the module docstring).
+    Query row i sits at position i + offset (offset = Nk - Nq, the reading
+    for fewer queries than keys in the module docstring; 0 when the lengths
+    are equal). causal: j <= i ([P3] 1.1 lower-triangular mask). window
+    (left, right): j >= i - left and j <= i + right, each side only when
+    >= 0 (the reading of [P1] 10.1 ``window_size``), with i the position.
     """
     left, right = _check_window(window)
-    i = np.asarray(rows, dtype=np.int64)[:, None]
+    i = np.asarray(rows, dtype=np.int64)[:, None] + int(offset)
     j = np.asarray(keys, dtype=np.int64)[None, :]
     ok = np.ones((i.shape[0], j.shape[1]), dtype=bool)
     if causal:
@@ -83,7 +97,7 @@ def scores_ref(q_bh, k_bh, scale, causal, rows=None, window=(-1, -1)):
     rows = np.arange(q_bh.shape[0]) if rows is None else np.asarray(rows, dtype=np.int64)
     s = float(scale) * (q_bh[rows] @ k_bh.T)
     if causal or tuple(window) != (-1, -1):
-        s = np.where(allowed_ref(rows, np.arange(n), causal, window), s, -np.inf)
+        s = np.where(allowed_ref(rows, np.arange(n), causal, window, n - q_bh.shape[0]), s, -np.inf)
     return s
 
 
@@ -94,23 +108,27 @@ def softmax_rows_ref(s):
     P_ij = exp(S_ij - m_i) / l_i. Masked (-inf) entries give exactly 0.
     """
     m = s.max(axis=1, keepdims=True)
-    e = np.exp(s - m)
+    empty = np.isneginf(m[:, 0])
+    e = np.exp(s - np.where(empty[:, None], 0.0, m))
     l = e.sum(axis=1, keepdims=True)
-    return e / l, m[:, 0], l[:, 0]
+    p = np.where(empty[:, None], 0.0, e / np.where(empty[:, None], 1.0, l))
+    return p, m[:, 0], l[:, 0]
 
 
 def attention_ref(q, k, v, scale, causal=False, rows=None, chunk=1024, window=(-1, -1)):
     """Plain three-step attention: O = softmax(scale Q K^T [+ mask]) V, and LSE.
 
     [P3] 1.1 (QK^T, mask + softmax, times V), [P2] 2 and [P5]
-    ``standard_attention``. Returns (O, LSE) as float64 arrays of shape
-    [B, H, R, d] and [B, H, R], where R is the number of selected query rows
-    (all N by default). Query rows are processed ``chunk`` at a time only to
-    bound memory; each chunk is the same untiled computation over all keys.
-    LSE_i = m_i + ln l_i = ln sum_j exp(S_ij).
+    ``standard_attention``. q is [B, H, Nq, d] and k, v are [B, H, Nk, d]
+    (Nk = Nq unless a key/value cache is longer; see the module docstring
+    for where the queries then sit). Returns (O, LSE) as float64 arrays of
+    shape [B, H, R, d] and [B, H, R], where R is the number of selected query
+    rows (all Nq by default). Query rows are processed ``chunk`` at a time
+    only to bound memory; each chunk is the same untiled computation over all
+    keys. LSE_i = m_i + ln l_i = ln sum_j exp(S_ij).
     """
     q, k, v = _f64(q), _f64(k), _f64(v)
-    _check(q, k, v)
+    _check_kv(q, k, v)
     B, H, N, D = q.shape
     rows = np.arange(N) if rows is None else np.asarray(rows, dtype=np.int64)
     R = rows.shape[0]
@@ -123,7 +141,7 @@ def attention_ref(q, k, v, scale, causal=False, rows=None, chunk=1024, window=(-
                 s = scores_ref(q[b, h], k[b, h], scale, causal, rr, window)
                 p, m, l = softmax_rows_ref(s)
                 out[b, h, c0:c0 + chunk] = p @ v[b, h]
-                lse[b, h, c0:c0 + chunk] = m + np.log(l)
+                lse[b, h, c0:c0 + chunk] = np.where(np.isneginf(m), -np.inf, m + np.log(np.where(l > 0, l, 1.0)))
     return out, lse
 
 

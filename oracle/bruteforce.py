@@ -17,17 +17,19 @@ import numpy as np
 def attention_bruteforce(q, k, v, scale, causal=False, digits=40, window=(-1, -1)):
     """Return (O, LSE) as float64 arrays, computed in Decimal at ``digits``.
 
-    Every float input converts to Decimal exactly. A masked key (causal and
-    j > i, or outside the window: j < i - left for left >= 0, j > i + right
-    for right >= 0) is left out of both sums, which is what a -inf score
-    means.
+    Every float input converts to Decimal exactly. k and v may hold more rows
+    (Nk) than q (Nq): query i then sits at position p = i + Nk - Nq, the last
+    Nq positions of the sequence. A masked key (causal and j > p, or outside
+    the window: j < p - left for left >= 0, j > p + right for right >= 0) is
+    left out of both sums, which is what a -inf score means.
     """
     left, right = int(window[0]), int(window[1])
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
     B, H, N, D = q.shape
-    if N > 64:
+    NK = k.shape[2]
+    if N > 64 or NK > 64:
         raise ValueError("brute force is for tiny inputs only")
     out = np.empty((B, H, N, D))
     lse = np.empty((B, H, N))
@@ -37,13 +39,14 @@ def attention_bruteforce(q, k, v, scale, causal=False, digits=40, window=(-1, -1
         for b in range(B):
             for h in range(H):
                 for i in range(N):
+                    pos = i + NK - N
                     weights = []
-                    for j in range(N):
-                        if causal and j > i:
+                    for j in range(NK):
+                        if causal and j > pos:
                             continue
-                        if left >= 0 and i - j > left:
+                        if left >= 0 and pos - j > left:
                             continue
-                        if right >= 0 and j - i > right:
+                        if right >= 0 and j - pos > right:
                             continue
                         dot = sum((Decimal(float(q[b, h, i, c])) * Decimal(float(k[b, h, j, c]))
                                    for c in range(D)), Decimal(0))

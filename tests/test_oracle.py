@@ -411,3 +411,65 @@ def test_window_rejects_sides_below_minus_one():
     q = rnd((1, 1, 4, 2), 91)
     with pytest.raises(ValueError):
         attention_ref(q, q, q, 1.0, False, window=(-2, 0))
+
+
+# --------------------------------------- fewer queries than keys (Nq < Nk) --
+
+RECT_CASES = [(c, w, nq, nk) for c, w in ((False, (-1, -1)), (True, (-1, -1)), (False, (2, 1)), (True, (3, -1)))
+              for nq, nk in ((1, 7), (3, 8), (5, 5), (6, 2))
+              if nq <= nk or (not c and w == (-1, -1))]  # Nq > Nk with a mask leaves rows without keys
+
+
+@pytest.mark.parametrize("causal,window,nq,nk", RECT_CASES)
+def test_rectangular_against_bruteforce(causal, window, nq, nk):
+    """q [.., Nq, d] against k, v [.., Nk, d]: the queries are the last Nq
+    positions. (Rows without keys: test_rectangular_rows_without_keys.)"""
+    rng = np.random.default_rng(nq * 10 + nk)
+    q = rng.standard_normal((1, 2, nq, 3))
+    k = rng.standard_normal((1, 2, nk, 3))
+    v = rng.standard_normal((1, 2, nk, 3))
+    o, lse = attention_ref(q, k, v, 0.7, causal, window=window)
+    ob, lb = attention_bruteforce(q, k, v, 0.7, causal, window=window)
+    np.testing.assert_allclose(o, ob, rtol=0, atol=1e-14)
+    np.testing.assert_allclose(lse, lb, rtol=0, atol=1e-14)
+
+
+@pytest.mark.parametrize("causal,window", [(True, (-1, -1)), (False, (40, 3)), (True, (17, -1)), (False, (-1, -1))])
+def test_rectangular_is_the_last_rows_of_the_square_problem(causal, window):
+    """Attention of the last Nq queries against all Nk keys equals rows
+    Nk - Nq .. Nk - 1 of the square problem (bottom-right placement)."""
+    rng = np.random.default_rng(5)
+    nk, nq = 150, 37
+    q = rng.standard_normal((2, 2, nk, 16))
+    k = rng.standard_normal((2, 2, nk, 16))
+    v = rng.standard_normal((2, 2, nk, 16))
+    o_sq, l_sq = attention_ref(q, k, v, 0.25, causal, window=window)
+    o_r, l_r = attention_ref(q[:, :, nk - nq:], k, v, 0.25, causal, window=window)
+    np.testing.assert_allclose(o_r, o_sq[:, :, nk - nq:], rtol=0, atol=1e-15)
+    np.testing.assert_allclose(l_r, l_sq[:, :, nk - nq:], rtol=0, atol=1e-15)
+
+
+def test_rectangular_single_query_sees_every_key_when_causal():
+    rng = np.random.default_rng(6)
+    q = rng.standard_normal((1, 1, 1, 8))
+    k = rng.standard_normal((1, 1, 40, 8))
+    v = rng.standard_normal((1, 1, 40, 8))
+    a = attention_ref(q, k, v, 0.3, True)
+    b = attention_ref(q, k, v, 0.3, False)
+    np.testing.assert_array_equal(a[0], b[0])
+    np.testing.assert_array_equal(a[1], b[1])
+
+
+def test_rectangular_rows_without_keys():
+    """Nq > Nk with a causal mask: query i sits at position i - (Nq - Nk),
+    so the first Nq - Nk rows see no key: O = 0, LSE = -inf. The others
+    equal the square problem on the last Nk queries."""
+    rng = np.random.default_rng(7)
+    q = rng.standard_normal((1, 1, 10, 4))
+    k = rng.standard_normal((1, 1, 6, 4))
+    v = rng.standard_normal((1, 1, 6, 4))
+    o, lse = attention_ref(q, k, v, 0.5, True)
+    assert (o[0, 0, :4] == 0).all() and np.isneginf(lse[0, 0, :4]).all()
+    o_sq, l_sq = attention_ref(q[:, :, 4:], k, v, 0.5, True)
+    np.testing.assert_array_equal(o[:, :, 4:], o_sq)
+    np.testing.assert_array_equal(lse[:, :, 4:], l_sq)
