@@ -341,6 +341,51 @@ def bench_graph(fa, inputs, dev, stream):
     return out
 
 
+def bench_decode(fa, inputs, dev, stream, steps, warmup, no_parity):
+    """A decode step: one new query per head against a key/value cache
+    (B=1, H=32, Nk=32768, d=128, bf16, causal), split-KV with the library's
+    choice of parts. HBM-bound: reported as GB/s of algorithmic bytes (K and
+    V read once, plus q, o and lse) against the 8 TB/s peak."""
+    import numpy as np
+    import torch
+
+    B, H, N, Nk, D = 1, 32, 1, 32768, 128
+    log(f"[bench] decode: B={B} H={H} N={N} Nk={Nk} d={D}: inputs")
+    q = inputs.make_qkv(B, H, N, D, "bf16", seed=42)[0]
+    _, k, v = inputs.make_qkv(B, H, Nk, D, "bf16", seed=43)
+    qd, kd, vd = (t.to(dev) for t in (q, k, v))
+    o = torch.empty_like(qd)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    splits = fa.splitkv_num_splits(B, H, N, D, True, dtype=fa.FA_BF16, Nk=Nk)
+    ws = torch.empty(max(fa.splitkv_workspace_bytes(B, H, N, D, splits), 16), dtype=torch.uint8, device=dev)
+
+    def step():
+        fa.fwd(qd, kd, vd, causal=True, out=o, lse=lse, num_splits=splits, workspace=ws)
+
+    ok, err_o, err_l = None, float("nan"), float("nan")
+    if not no_parity:
+        from oracle import attention_ref
+
+        o.fill_(float("nan"))
+        step()
+        torch.cuda.synchronize()
+        o_ref, l_ref = attention_ref(q.double().numpy(), k.double().numpy(), v.double().numpy(),
+                                     1.0 / math.sqrt(D), True)
+        err_o = float(np.abs(o.double().cpu().numpy() - o_ref).max())
+        err_l = float(np.abs(lse.double().cpu().numpy() - l_ref).max())
+        ok = err_o <= 1e-2 and err_l <= 1e-3
+        log(f"[bench] decode: max|dO|={err_o:.3e} max|dLSE|={err_l:.3e} parity={'ok' if ok else 'FAIL'}")
+    _, per = time_launches(step, stream, steps, warmup)
+    kms = float(np.mean(per))
+    nbytes = B * H * (2 * Nk * D * 2 + 2 * N * D * 2 + N * 4)
+    gbs = nbytes / (kms * 1e-3) / 1e9
+    return {"workload": "decode step: B=1 H=32 N=1 against Nk=32768, d=128 bf16 causal", "num_splits": splits,
+            "kernel_ms_mean": round(kms, 4), "bound": "hbm", "achieved_GBps": round(gbs, 1),
+            "peak_GBps": 8000.0, "frac": round(gbs / 8000.0, 4), "algorithmic_bytes": nbytes,
+            "timed": "fwd kernel + merge kernel per call", "parity_ok": ok, "max_abs_dO": err_o,
+            "max_abs_dLSE": err_l}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -500,6 +545,7 @@ def main():
         out["backward_d256"] = bench_backward_d256(fa, inputs, dev, stream, 5, 2)
         out["packed"] = bench_packed(fa, inputs, dev, stream, max(args.steps, 20), args.warmup)
         out["graph"] = bench_graph(fa, inputs, dev, stream)
+        out["decode"] = bench_decode(fa, inputs, dev, stream, max(args.steps, 20), args.warmup, args.no_parity)
         out["splitkv"] = bench_splitkv(fa, inputs, dev, stream, max(args.steps, 20), args.warmup, args.no_parity)
     if args.calibrate_copy:
         log("[bench] copy calibration: 3 x 1 GiB device-to-device copy")
@@ -514,7 +560,7 @@ def main():
         out["cpu_baseline"] = cpu_baseline(q, k, v, scale, True, args.cpu_heads)
     print(json.dumps(out), flush=True)
     failed = [par["ok"]] + [out[k]["parity_ok"] for k in ("secondary", "fp32", "window", "backward", "packed",
-                                                          "splitkv")
+                                                          "splitkv", "decode")
                           if k in out]
     if "backward_d256" in out:
         failed.append(out["backward_d256"]["all_finite"])

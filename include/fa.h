@@ -177,6 +177,31 @@ int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* 
                    int window_left, int window_right, int dtype, void* stream);
 
 /*
+ * fa_fwd_kv - the general forward: fa_fwd_splitkv with N query rows against
+ * Nk key/value rows, for new tokens attending to a key/value cache (the
+ * inference use of section 11.2 of the flash-attn 2.8.3 build guide,
+ * intelliparadigm.com, which gives no definition for unequal lengths).
+ *
+ * q, o, lse have N rows per (b, h); k and v have Nk rows (their strides, in
+ * the strides array as for fa_fwd_strided, describe [B, H, Nk, d] views).
+ * The N queries are the last N positions of the Nk-long sequence: query
+ * row i sits at position p = i + Nk - N, and the causal mask (key j <= p)
+ * and the window (p - window_left <= j <= p + window_right) apply to p. With
+ * N = Nk this is fa_fwd_splitkv. A decode step is N = 1 (or a few rows)
+ * against a long Nk, typically with num_splits = 0 so that the key range is
+ * spread over the GPU.
+ *
+ * Errors as fa_fwd_splitkv, and: FA_ERR_SHAPE for Nk < 0 or too large;
+ * FA_ERR_ARG when some query row would see no key: Nk = 0 (with N > 0), or
+ * N > Nk together with a causal mask or a window (rows before the first key
+ * position). Workspace bytes depend on N only (fa_fwd_splitkv_workspace).
+ */
+int fa_fwd_kv(const void* q, const void* k, const void* v, void* o, float* lse,
+              const long long* strides, void* workspace, long long workspace_bytes,
+              int num_splits, int B, int H, int N, int Nk, int d, float scale, int causal,
+              int window_left, int window_right, int dtype, void* stream);
+
+/*
  * fa_fwd_num_splits - host-only: the number of parts fa_fwd_splitkv uses
  * for num_splits = 0: 1 when the plain grid already fills half the GPU;
  * otherwise enough parts to fill it, at most 16, while each part of the
@@ -189,6 +214,9 @@ int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* 
  */
 int fa_fwd_num_splits(int B, int H, int N, int d, int causal, int window_left,
                       int window_right, int dtype, int* num_splits);
+/* fa_fwd_kv_num_splits - the same for N query rows against Nk keys (fa_fwd_kv). */
+int fa_fwd_kv_num_splits(int B, int H, int N, int Nk, int d, int causal, int window_left,
+                         int window_right, int dtype, int* num_splits);
 int fa_fwd_splitkv_workspace(int B, int H, int N, int d, int num_splits, long long* bytes);
 
 /*

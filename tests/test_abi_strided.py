@@ -290,3 +290,31 @@ def test_splitkv_heuristic():
 ])
 def test_splitkv_errors(ws, ws_bytes, splits, code):
     assert splitkv(ws, ws_bytes, splits) == code
+
+
+# ----------------------------------------------- queries against a cache --
+
+def fwd_kv(N, Nk, causal=0, left=-1, right=-1, B=1, H=2, d=64):
+    ptrs = [0x100_0000, 0x200_0000, 0x300_0000, 0x400_0000]
+    return fa.fa_fwd_kv(*ptrs, 0x7000_0000, None, None, 0, 1, B, H, N, Nk, d, 0.125, causal, left, right,
+                        fa.FA_BF16)
+
+
+@pytest.mark.parametrize("N,Nk,causal,left,right,code", [
+    (5, -1, 0, -1, -1, SHAPE),
+    (5, 1 << 30, 0, -1, -1, SHAPE),
+    (5, 0, 0, -1, -1, ARG),       # no key at all
+    (8, 4, 1, -1, -1, ARG),       # causal: rows 0..3 sit before the first key
+    (8, 4, 0, 2, -1, ARG),        # window: the same
+    (8, 4, 0, -1, 0, ARG),
+    (0, 0, 1, -1, -1, OK),        # nothing to do
+])
+def test_fwd_kv_checks(N, Nk, causal, left, right, code):
+    assert fwd_kv(N, Nk, causal, left, right) == code
+
+
+def test_fwd_kv_num_splits_for_decode():
+    # one query per head against a long cache: the key range is spread out
+    assert fa.splitkv_num_splits(1, 32, 1, 128, True, Nk=32768) == 16
+    assert fa.splitkv_num_splits(1, 32, 1, 128, True, Nk=256) == 1
+    assert fa.splitkv_num_splits(4, 64, 2048, 128, True, Nk=4096) == 1

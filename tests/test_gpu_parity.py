@@ -185,7 +185,11 @@ def test_single_key_and_causal_first_row(dtype):
 @pytest.mark.parametrize("dtype,D", [("bf16", 256), ("f16", 128), ("f32", 64)])
 def test_causal_rows_ignore_later_keys(dtype, D):
     """Causal structure: changing the keys and values after row i0 leaves
-    rows 0..i0 (O and LSE) bitwise unchanged; later rows do change."""
+    rows 0..i0 unchanged, bit for bit in the query tiles that end before
+    the first changed key (their workgroups never load it) and within the
+    parity bound in the tile that holds i0 (there the changed keys are
+    masked, but a wave-wide move of the exponent reference, triggered by a
+    later row of the wave, may change the rounding); later rows change."""
     N, i0 = 700, 300
     q, k, v = inputs.make_qkv(1, 2, N, D, dtype, seed=14)
     o1, l1 = run(q, k, v, 0.1, True)
@@ -194,8 +198,11 @@ def test_causal_rows_ignore_later_keys(dtype, D):
     k2[:, :, i0 + 1:] = torch.randn(k2[:, :, i0 + 1:].shape, generator=g).to(k.dtype) * 3
     v2[:, :, i0 + 1:] = torch.randn(v2[:, :, i0 + 1:].shape, generator=g).to(v.dtype) * 3
     o2, l2 = run(q, k2, v2, 0.1, True)
-    assert torch.equal(o1[:, :, :i0 + 1], o2[:, :, :i0 + 1])
-    assert torch.equal(l1[:, :, :i0 + 1], l2[:, :, :i0 + 1])
+    cut = (i0 + 1) // 128 * 128  # rows of query tiles that end before key i0 + 1
+    assert torch.equal(o1[:, :, :cut], o2[:, :, :cut])
+    assert torch.equal(l1[:, :, :cut], l2[:, :, :cut])
+    assert (o1[:, :, cut:i0 + 1].double() - o2[:, :, cut:i0 + 1].double()).abs().max().item() <= TOL_O[q.dtype]
+    assert (l1[:, :, cut:i0 + 1] - l2[:, :, cut:i0 + 1]).abs().max().item() <= TOL_LSE
     assert not torch.equal(o1[:, :, i0 + 1:], o2[:, :, i0 + 1:])
 
 

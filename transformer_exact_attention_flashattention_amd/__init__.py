@@ -64,7 +64,7 @@ STATUS = {
 # Every symbol include/fa.h declares.
 EXPORTS = ("fa_fwd", "fa_fwd_window", "fa_fwd_strided", "fa_bwd", "fa_bwd_strided", "fa_strerror",
            "fa_fwd_grid", "fa_fwd_strided_check", "fa_bwd_strided_check", "fa_fwd_splitkv",
-           "fa_fwd_num_splits", "fa_fwd_splitkv_workspace")
+           "fa_fwd_num_splits", "fa_fwd_splitkv_workspace", "fa_fwd_kv", "fa_fwd_kv_num_splits")
 
 _lib = None
 
@@ -118,6 +118,14 @@ def lib() -> ctypes.CDLL:
             ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_float,
             ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
         ]
+        h.fa_fwd_kv.restype = ctypes.c_int
+        h.fa_fwd_kv.argtypes = [ctypes.c_void_p] * 5 + [
+            ctypes.POINTER(ctypes.c_longlong), ctypes.c_void_p, ctypes.c_longlong, ctypes.c_int,
+            ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_float,
+            ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+        ]
+        h.fa_fwd_kv_num_splits.restype = ctypes.c_int
+        h.fa_fwd_kv_num_splits.argtypes = [ctypes.c_int] * 9 + [ctypes.POINTER(ctypes.c_int)]
         h.fa_fwd_num_splits.restype = ctypes.c_int
         h.fa_fwd_num_splits.argtypes = [ctypes.c_int] * 8 + [ctypes.POINTER(ctypes.c_int)]
         h.fa_fwd_splitkv_workspace.restype = ctypes.c_int
@@ -177,11 +185,20 @@ def fa_fwd_splitkv(q, k, v, o, lse, strides, workspace, workspace_bytes, num_spl
                                 B, H, N, d, scale, causal, window_left, window_right, dtype, stream)
 
 
-def splitkv_num_splits(B, H, N, d, causal=False, window_size=(-1, -1), dtype=FA_BF16):
-    """The number of key-range parts fa_fwd_splitkv picks by itself."""
+def fa_fwd_kv(q, k, v, o, lse, strides, workspace, workspace_bytes, num_splits, B, H, N, Nk, d, scale, causal,
+              window_left, window_right, dtype, stream=None) -> int:
+    """Raw call of the general forward: N query rows against Nk key rows."""
+    return lib().fa_fwd_kv(q, k, v, o, lse, _strides_arg(strides, 12), workspace, workspace_bytes, num_splits,
+                           B, H, N, Nk, d, scale, causal, window_left, window_right, dtype, stream)
+
+
+def splitkv_num_splits(B, H, N, d, causal=False, window_size=(-1, -1), dtype=FA_BF16, Nk=None):
+    """The number of key-range parts the split-KV forward picks by itself
+    (for N queries against Nk keys; Nk defaults to N)."""
     left, right = _window(window_size)
     n = ctypes.c_int(0)
-    st = lib().fa_fwd_num_splits(B, H, N, d, int(bool(causal)), left, right, dtype, ctypes.byref(n))
+    nk = N if Nk is None else int(Nk)
+    st = lib().fa_fwd_kv_num_splits(B, H, N, nk, d, int(bool(causal)), left, right, dtype, ctypes.byref(n))
     if st != 0:
         raise FaError(st, strerror(st))
     return n.value
@@ -295,18 +312,24 @@ def fwd(q, k, v, softmax_scale=None, causal=False, window_size=(-1, -1), out=Non
     """Attention forward on the GPU: returns (o [B,H,N,d], lse [B,H,N] fp32).
 
     q, k, v (and ``out`` if given) may be strided views; a new ``out`` is
-    contiguous. ``num_splits`` > 1 splits every query tile's keys into that
-    many parts merged by log-sum-exp (fa_fwd_splitkv); 0 lets the library
-    choose; the workspace (a GPU tensor of at least
-    ``splitkv_workspace_bytes`` bytes) is allocated when not given."""
+    contiguous. k and v may have more rows than q ([B, H, Nk, d], a key/value
+    cache): the queries are then the last N positions (fa_fwd_kv).
+    ``num_splits`` > 1 splits every query tile's keys into that many parts
+    merged by log-sum-exp; 0 lets the library choose; the workspace (a GPU
+    tensor of at least ``splitkv_workspace_bytes`` bytes) is allocated when
+    not given."""
     import torch
 
     left, right = _window(window_size)
     _check_view("q", q, None, None, None)
     code = _dtype_code(q)
-    _check_view("k", k, q.shape, q.dtype, q.device)
-    _check_view("v", v, q.shape, q.dtype, q.device)
+    _check_view("k", k, None, q.dtype, q.device)
+    kv_shape = (q.shape[0], q.shape[1], k.shape[2], q.shape[3])
+    if tuple(k.shape) != kv_shape:
+        raise ValueError(f"k must be [B, H, Nk, d] with q's B, H, d: q {tuple(q.shape)}, k {tuple(k.shape)}")
+    _check_view("v", v, kv_shape, q.dtype, q.device)
     B, H, N, d = q.shape
+    Nk = k.shape[2]
     if d not in (64, 128, 256):
         raise NotImplementedError(f"head dimension {d} is not supported (64, 128, 256)")
     scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
@@ -318,24 +341,25 @@ def fwd(q, k, v, softmax_scale=None, causal=False, window_size=(-1, -1), out=Non
     _check_rowstat("lse", lse, B, H, N, q.device)
     splits = int(num_splits)
     if splits == 0:
-        splits = splitkv_num_splits(B, H, N, d, causal, (left, right), code)
+        splits = splitkv_num_splits(B, H, N, d, causal, (left, right), code, Nk=Nk)
     with torch.cuda.device(q.device):
         stream = torch.cuda.current_stream().cuda_stream
-        if splits == 1:
+        if splits == 1 and Nk == N:
             st = fa_fwd_strided(
                 q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), _strides(q, k, v, out),
                 B, H, N, d, scale, int(bool(causal)), left, right, code, stream,
             )
         else:
             need = splitkv_workspace_bytes(B, H, N, d, splits)
-            if workspace is None:
+            if workspace is None and need > 0:
                 workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-            if not workspace.is_cuda or workspace.device != q.device:
+            if workspace is not None and (not workspace.is_cuda or workspace.device != q.device):
                 raise ValueError("workspace must be on q's device")
-            st = fa_fwd_splitkv(
+            ws_ptr = workspace.data_ptr() if workspace is not None else None
+            ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+            st = fa_fwd_kv(
                 q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), _strides(q, k, v, out),
-                workspace.data_ptr(), workspace.numel() * workspace.element_size(), splits,
-                B, H, N, d, scale, int(bool(causal)), left, right, code, stream,
+                ws_ptr, ws_bytes, splits, B, H, N, Nk, d, scale, int(bool(causal)), left, right, code, stream,
             )
     if st != 0:
         raise FaError(st, strerror(st))
@@ -418,6 +442,8 @@ def _autograd_functions():
             def backward(ctx, do):
                 q, k, v, o, lse = ctx.saved_tensors
                 softmax_scale, causal, window_size, bnhd = ctx.args
+                if k.shape != q.shape:
+                    raise NotImplementedError("the backward pass needs equal query and key lengths")
                 t = (lambda x: x.transpose(1, 2)) if bnhd else (lambda x: x)
                 grads = [torch.empty(q.shape, dtype=q.dtype, device=q.device) for _ in range(3)]
                 bwd(t(q), t(k), t(v), t(o), lse, t(_last_dim_contiguous(do)), softmax_scale=softmax_scale,
@@ -482,8 +508,10 @@ def flash_attn_qkvpacked_func(qkv, dropout_p=0.0, softmax_scale=None, causal=Fal
 
 def flash_attn_func(q, k, v, dropout_p=0.0, softmax_scale=None, causal=False, window_size=(-1, -1),
                     alibi_slopes=None, deterministic=False):
-    """Attention for q, k, v [B, N, H, d] -> o [B, N, H, d], differentiable;
-    inputs are read in place (any strides with a contiguous last dimension)."""
+    """Attention for q [B, N, H, d] and k, v [B, Nk, H, d] -> o [B, N, H, d],
+    differentiable when Nk = N; inputs are read in place (any strides with a
+    contiguous last dimension). With Nk > N the queries are the last N
+    positions (a key/value cache)."""
     _no_dropout(dropout_p, alibi_slopes)
     for name, t in (("q", q), ("k", k), ("v", v)):
         if t.dim() != 4:

@@ -15,9 +15,9 @@
 namespace {
 
 typedef void (*fwd16_fn)(const uint16_t*, const uint16_t*, const uint16_t*, uint16_t*, float*, fa::View,
-                         fa::View, fa::View, fa::View, int, int, int, int, float, int, int, fa::SplitOut);
+                         fa::View, fa::View, fa::View, int, int, int, int, int, float, int, int, fa::SplitOut);
 typedef void (*fwd32_fn)(const float*, const float*, const float*, float*, float*, fa::View, fa::View,
-                         fa::View, fa::View, int, int, int, int, float, int, int, fa::SplitOut);
+                         fa::View, fa::View, int, int, int, int, int, float, int, int, fa::SplitOut);
 
 template <class T>
 fwd16_fn pick16(int d, bool causal) {
@@ -83,8 +83,8 @@ extern "C" const char* fa_strerror(int status) {
     case FA_ERR_ALIGN:
       return "q, k, v, o (and every row of their views) must be 16-byte aligned and lse 4-byte aligned";
     case FA_ERR_ARG:
-      return "causal must be 0 or 1, scale finite, window sides >= -1, and outputs must not overlap "
-             "inputs, each other or themselves";
+      return "causal must be 0 or 1, scale finite, window sides >= -1, every query row must see a key, "
+             "and outputs must not overlap inputs, each other or themselves";
     case FA_ERR_LAUNCH: return "the HIP runtime rejected the kernel launch";
   }
   return "unknown fa_status";
@@ -111,22 +111,30 @@ struct FwdPlan {
   fa::View view[4];
 };
 
+// N query rows against Nk key rows (the queries are the last N positions).
 int plan_fwd(const void* q, const void* k, const void* v, void* o, float* lse, const long long* strides, int B,
-             int H, int N, int d, float scale, int causal, int window_left, int window_right, int dtype,
+             int H, int N, int Nk, int d, float scale, int causal, int window_left, int window_right, int dtype,
              FwdPlan* plan) {
   int st = check_shape(B, H, N, d, causal, dtype, &plan->nblocks, &plan->nqt);
   if (st != FA_OK) return st;
+  if (Nk < 0 || Nk > (1 << 30) - fa::kBr) return FA_ERR_SHAPE;
   if (!std::isfinite(scale)) return FA_ERR_ARG;
   if (window_left < -1 || window_right < -1) return FA_ERR_ARG;
   if (plan->nblocks == 0) return FA_OK;  // B*H*N == 0: nothing to do
+  // Every query row must see a key: some key at all, and with a causal
+  // mask or a window no query before the first key position.
+  if (Nk == 0) return FA_ERR_ARG;
+  if (N > Nk && (causal || window_left >= 0 || window_right >= 0)) return FA_ERR_ARG;
   if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
   if ((uintptr_t)lse & 3) return FA_ERR_ALIGN;
 
   const fa::host::Dims g{B, H, N, d, dtype == FA_F32 ? 4 : 2};
+  const fa::host::Dims gk{B, H, Nk, d, g.esz};
   const void* ptrs[4] = {q, k, v, o};
   fa::host::Operand op[4];
   for (int i = 0; i < 4; ++i) {
-    st = fa::host::make_operand(ptrs[i], strides ? strides + 3 * i : nullptr, g, &op[i], &plan->view[i]);
+    st = fa::host::make_operand(ptrs[i], strides ? strides + 3 * i : nullptr, (i == 1 || i == 2) ? gk : g, &op[i],
+                                &plan->view[i]);
     if (st != FA_OK) return st;
   }
   const long long lbytes = (long long)B * H * N * (long long)sizeof(float);
@@ -144,7 +152,7 @@ extern "C" int fa_fwd_strided_check(const void* q, const void* k, const void* v,
                                     const long long* strides, int B, int H, int N, int d, float scale,
                                     int causal, int window_left, int window_right, int dtype) {
   FwdPlan plan;
-  return plan_fwd(q, k, v, o, lse, strides, B, H, N, d, scale, causal, window_left, window_right, dtype, &plan);
+  return plan_fwd(q, k, v, o, lse, strides, B, H, N, N, d, scale, causal, window_left, window_right, dtype, &plan);
 }
 
 namespace {
@@ -163,11 +171,11 @@ constexpr int kMinTiles = 32;
 // Parts for a grid of nblocks workgroups: none while the grid fills half
 // the chip; otherwise enough to fill it, as long as each part of the widest
 // query tile keeps the minimum number of key tiles; at most 16.
-int choose_splits(long long nblocks, int N, int d, int causal, int wl, int wr, int dtype) {
+int choose_splits(long long nblocks, int Nk, int d, int causal, int wl, int wr, int dtype) {
   const int slots = resident_blocks(d, dtype);
   if (nblocks * 2 > slots) return 1;
-  long long span = (long long)rows_per_block(dtype) + (wl < 0 ? N : wl) + (causal || wr == 0 ? 0 : (wr < 0 ? N : wr));
-  span = std::min<long long>(span, N);
+  long long span = (long long)rows_per_block(dtype) + (wl < 0 ? Nk : wl) + (causal || wr == 0 ? 0 : (wr < 0 ? Nk : wr));
+  span = std::min<long long>(span, Nk);
   const int tiles = (int)((span + fa::kBc - 1) / fa::kBc);
   int s = (int)(slots / std::max<long long>(nblocks, 1));
   s = std::min(s, tiles / (causal ? kMinTilesCausal : kMinTiles));
@@ -183,14 +191,14 @@ long long workspace_bytes_for(int B, int H, int N, int d, int nsplit) {
 // Enqueues the forward kernel (and, with a split, the merge) for a plan
 // that passed plan_fwd.
 int launch_fwd(const FwdPlan& plan, const void* q, const void* k, const void* v, void* o, float* lse, int B,
-               int H, int N, int d, float scale, int causal, int window_left, int window_right, int dtype,
+               int H, int N, int Nk, int d, float scale, int causal, int window_left, int window_right, int dtype,
                float* part, int nsplit, hipStream_t stream) {
   // log2(e) is folded into the scale: exp(x * scale) == exp2(x * c).
   const float c = (float)((double)scale * 1.4426950408889634074);
-  int h_arg = H, n_arg = N, nqt_arg = plan.nqt, nb_arg = (int)plan.nblocks;
+  int h_arg = H, n_arg = N, nk_arg = Nk, nqt_arg = plan.nqt, nb_arg = (int)plan.nblocks;
   float c_arg = c;
-  // Visible keys of query i: i - wl .. i + wr, an unbounded side as 2^30
-  // (N is below 2^30, so no sum of a row index and a side overflows).
+  // Visible keys of the query at position p: p - wl .. p + wr, an unbounded
+  // side as 2^30 (positions are below 2^30, so no sum with a side overflows).
   constexpr int kUnbounded = 1 << 30;
   int wl = window_left < 0 ? kUnbounded : window_left;
   int wr = window_right < 0 ? kUnbounded : window_right;
@@ -199,8 +207,8 @@ int launch_fwd(const FwdPlan& plan, const void* q, const void* k, const void* v,
   fa::SplitOut sp{nsplit > 1 ? part : nullptr, nsplit > 1 ? nsplit : 1, B * H};
   void* args[] = {(void*)&q,       (void*)&k,       (void*)&v,       (void*)&o,     (void*)&lse,
                   (void*)&view[0], (void*)&view[1], (void*)&view[2], (void*)&view[3], (void*)&h_arg,
-                  (void*)&n_arg,   (void*)&nqt_arg, (void*)&nb_arg,  (void*)&c_arg, (void*)&wl,
-                  (void*)&wr,      (void*)&sp};
+                  (void*)&n_arg,   (void*)&nk_arg,  (void*)&nqt_arg, (void*)&nb_arg,  (void*)&c_arg,
+                  (void*)&wl,      (void*)&wr,      (void*)&sp};
 
   const void* fn = nullptr;
   const void* merge = nullptr;
@@ -236,26 +244,69 @@ int launch_fwd(const FwdPlan& plan, const void* q, const void* k, const void* v,
 
 }  // namespace
 
+namespace {
+
+int fwd_general(const void* q, const void* k, const void* v, void* o, float* lse, const long long* strides,
+                void* workspace, long long workspace_bytes, int num_splits, int B, int H, int N, int Nk, int d,
+                float scale, int causal, int window_left, int window_right, int dtype, void* stream) {
+  if (num_splits < 0 || num_splits > kMaxSplits) return FA_ERR_ARG;
+  FwdPlan plan;
+  int st =
+      plan_fwd(q, k, v, o, lse, strides, B, H, N, Nk, d, scale, causal, window_left, window_right, dtype, &plan);
+  if (st != FA_OK || plan.nblocks == 0) return st;
+  int ns = num_splits == 0 ? choose_splits(plan.nblocks, Nk, d, causal, window_left, window_right, dtype)
+                           : num_splits;
+  float* part = nullptr;
+  if (ns > 1) {
+    const long long need = workspace_bytes_for(B, H, N, d, ns);
+    if (!workspace) return FA_ERR_NULL;
+    if ((uintptr_t)workspace & 15) return FA_ERR_ALIGN;
+    if (workspace_bytes < need) return FA_ERR_ARG;
+    // The workspace is written: it may not overlap any operand.
+    const fa::host::Dims g{B, H, N, d, dtype == FA_F32 ? 4 : 2};
+    const fa::host::Dims gk{B, H, Nk, d, g.esz};
+    const void* ptrs[4] = {q, k, v, o};
+    for (int i = 0; i < 4; ++i) {
+      fa::host::Operand op;
+      fa::View unused;
+      st = fa::host::make_operand(ptrs[i], strides ? strides + 3 * i : nullptr, (i == 1 || i == 2) ? gk : g, &op,
+                                  &unused);
+      if (st != FA_OK) return st;
+      if (fa::host::ranges_overlap((uintptr_t)workspace, need, op.p, op.span)) return FA_ERR_ARG;
+    }
+    if (fa::host::ranges_overlap((uintptr_t)workspace, need, (uintptr_t)lse,
+                                 (long long)B * H * N * (long long)sizeof(float)))
+      return FA_ERR_ARG;
+    part = (float*)workspace;
+  }
+  return launch_fwd(plan, q, k, v, o, lse, B, H, N, Nk, d, scale, causal, window_left, window_right, dtype, part,
+                    ns, (hipStream_t)stream);
+}
+
+}  // namespace
+
 extern "C" int fa_fwd_strided(const void* q, const void* k, const void* v, void* o, float* lse,
                               const long long* strides, int B, int H, int N, int d, float scale, int causal,
                               int window_left, int window_right, int dtype, void* stream) {
-  FwdPlan plan;
-  const int st =
-      plan_fwd(q, k, v, o, lse, strides, B, H, N, d, scale, causal, window_left, window_right, dtype, &plan);
-  if (st != FA_OK || plan.nblocks == 0) return st;
-  return launch_fwd(plan, q, k, v, o, lse, B, H, N, d, scale, causal, window_left, window_right, dtype, nullptr, 1,
-                    (hipStream_t)stream);
+  return fwd_general(q, k, v, o, lse, strides, nullptr, 0, 1, B, H, N, N, d, scale, causal, window_left,
+                     window_right, dtype, stream);
 }
 
 extern "C" int fa_fwd_num_splits(int B, int H, int N, int d, int causal, int window_left, int window_right,
                                  int dtype, int* num_splits) {
+  return fa_fwd_kv_num_splits(B, H, N, N, d, causal, window_left, window_right, dtype, num_splits);
+}
+
+extern "C" int fa_fwd_kv_num_splits(int B, int H, int N, int Nk, int d, int causal, int window_left,
+                                    int window_right, int dtype, int* num_splits) {
   long long nblocks = 0;
   int nqt = 0;
   const int st = check_shape(B, H, N, d, causal, dtype, &nblocks, &nqt);
   if (st != FA_OK) return st;
+  if (Nk < 0 || Nk > (1 << 30) - fa::kBr) return FA_ERR_SHAPE;
   if (window_left < -1 || window_right < -1) return FA_ERR_ARG;
   if (!num_splits) return FA_ERR_NULL;
-  *num_splits = nblocks == 0 ? 1 : choose_splits(nblocks, N, d, causal, window_left, window_right, dtype);
+  *num_splits = nblocks == 0 || Nk == 0 ? 1 : choose_splits(nblocks, Nk, d, causal, window_left, window_right, dtype);
   return FA_OK;
 }
 
@@ -271,35 +322,16 @@ extern "C" int fa_fwd_splitkv(const void* q, const void* k, const void* v, void*
                               const long long* strides, void* workspace, long long workspace_bytes, int num_splits,
                               int B, int H, int N, int d, float scale, int causal, int window_left,
                               int window_right, int dtype, void* stream) {
-  if (num_splits < 0 || num_splits > kMaxSplits) return FA_ERR_ARG;
-  FwdPlan plan;
-  int st = plan_fwd(q, k, v, o, lse, strides, B, H, N, d, scale, causal, window_left, window_right, dtype, &plan);
-  if (st != FA_OK || plan.nblocks == 0) return st;
-  int ns = num_splits == 0 ? choose_splits(plan.nblocks, N, d, causal, window_left, window_right, dtype)
-                           : num_splits;
-  float* part = nullptr;
-  if (ns > 1) {
-    const long long need = workspace_bytes_for(B, H, N, d, ns);
-    if (!workspace) return FA_ERR_NULL;
-    if ((uintptr_t)workspace & 15) return FA_ERR_ALIGN;
-    if (workspace_bytes < need) return FA_ERR_ARG;
-    // The workspace is written: it may not overlap any operand.
-    const fa::host::Dims g{B, H, N, d, dtype == FA_F32 ? 4 : 2};
-    const void* ptrs[4] = {q, k, v, o};
-    for (int i = 0; i < 4; ++i) {
-      fa::host::Operand op;
-      fa::View unused;
-      st = fa::host::make_operand(ptrs[i], strides ? strides + 3 * i : nullptr, g, &op, &unused);
-      if (st != FA_OK) return st;
-      if (fa::host::ranges_overlap((uintptr_t)workspace, need, op.p, op.span)) return FA_ERR_ARG;
-    }
-    if (fa::host::ranges_overlap((uintptr_t)workspace, need, (uintptr_t)lse,
-                                 (long long)B * H * N * (long long)sizeof(float)))
-      return FA_ERR_ARG;
-    part = (float*)workspace;
-  }
-  return launch_fwd(plan, q, k, v, o, lse, B, H, N, d, scale, causal, window_left, window_right, dtype, part, ns,
-                    (hipStream_t)stream);
+  return fwd_general(q, k, v, o, lse, strides, workspace, workspace_bytes, num_splits, B, H, N, N, d, scale, causal,
+                     window_left, window_right, dtype, stream);
+}
+
+extern "C" int fa_fwd_kv(const void* q, const void* k, const void* v, void* o, float* lse, const long long* strides,
+                         void* workspace, long long workspace_bytes, int num_splits, int B, int H, int N, int Nk,
+                         int d, float scale, int causal, int window_left, int window_right, int dtype,
+                         void* stream) {
+  return fwd_general(q, k, v, o, lse, strides, workspace, workspace_bytes, num_splits, B, H, N, Nk, d, scale, causal,
+                     window_left, window_right, dtype, stream);
 }
 
 extern "C" int fa_fwd_window(const void* q, const void* k, const void* v, void* o, float* lse, int B,

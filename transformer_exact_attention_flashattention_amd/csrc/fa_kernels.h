@@ -157,8 +157,9 @@ __device__ __forceinline__ void decode_block(int nblocks, int nqt, bool causal, 
 }
 
 // One online-softmax update for the 16 scores a lane holds: the 32x32 MFMA
-// tile s of keys kb + [0, 32) (register r: key kb + acc_row(r, hh)) for query
-// row qrow, which sees keys qrow - wl .. qrow + wr below N. On return s
+// tile s of keys kb + [0, 32) (register r: key kb + acc_row(r, hh)) for the
+// query at position qrow, which sees keys qrow - wl .. qrow + wr below N
+// (q0: position of the wave's first row; N: number of keys). On return s
 // holds P = exp2(S*c - m_new), unrounded fp32; returns alpha =
 // exp2(m_old - m_new).
 __device__ __forceinline__ float online_softmax(f32x16& s, float c, int kb, int qrow, int q0, int N,
@@ -343,8 +344,8 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
                           amdgpu_waves_per_eu(D >= 256 ? 1 : 2, D >= 256 ? 1 : 2)))
 void fwd16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                   const uint16_t* __restrict__ V, uint16_t* __restrict__ O,
-                  float* __restrict__ LSE, View vq, View vk, View vv, View vo, int H, int N, int nqt,
-                  int nblocks, float c, int wl, int wr, SplitOut sp) {
+                  float* __restrict__ LSE, View vq, View vk, View vv, View vo, int H, int N, int Nk,
+                  int nqt, int nblocks, float c, int wl, int wr, SplitOut sp) {
   using G = Geo16<D>;
   typedef short s16x4 __attribute__((ext_vector_type(4)));
   typedef __attribute__((address_space(3))) s16x4* lds_s16x4_t;
@@ -369,6 +370,10 @@ void fwd16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K
   const int hh = lane >> 5;
   const int q0 = qt * kBr + wave * 32;
   const int qrow = q0 + n;
+  // Query row i sits at position i + Nk - N of the key sequence (the last
+  // N positions; 0 when the lengths are equal): masks use positions.
+  const int pos_off = Nk - N;
+  const int qpos = qrow + pos_off;
 
   // Q^T as B operands: lane (n, hh), k-step s holds Q[qrow][16s + 8hh .. +7].
   // A negative scale is folded into Q (an exact sign flip) so that c >= 0.
@@ -384,14 +389,14 @@ void fwd16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K
     qf[s] ^= qflip;
   }
 
-  // Key tiles the block needs: t_lo .. t_lo + nkt - 1 (query i sees keys
-  // i - wl .. i + wr; wr is 0 when causal, and an unbounded side is 2^30).
-  // Tiles full_lo .. full_hi are visible to every row of the block.
-  const int q_lo = qt * kBr;
-  int t_lo = max(q_lo - wl, 0) / kBc;
-  int nkt = min(min(q_lo + kBr - 1, N - 1) + wr, N - 1) / kBc + 1 - t_lo;
-  const int full_lo = (max(q_lo + kBr - 1 - wl, 0) + kBc - 1) / kBc;
-  const int full_hi = floor_div(min(N, q_lo + wr + 1) - kBc, kBc);
+  // Key tiles the block needs: t_lo .. t_lo + nkt - 1 (a query at position
+  // p sees keys p - wl .. p + wr; wr is 0 when causal, and an unbounded side
+  // is 2^30). Tiles full_lo .. full_hi are visible to every row of the block.
+  const int p_lo = qt * kBr + pos_off;  // position of the block's first row
+  int t_lo = max(p_lo - wl, 0) / kBc;
+  int nkt = min(min(qt * kBr + kBr - 1, N - 1) + pos_off + wr, Nk - 1) / kBc + 1 - t_lo;
+  const int full_lo = (max(p_lo + kBr - 1 - wl, 0) + kBc - 1) / kBc;
+  const int full_hi = floor_div(min(Nk, p_lo + wr + 1) - kBc, kBc);
   if (sp.part) {
     split_range(blockIdx.y, sp.nsplit, t_lo, nkt);
     if (nkt == 0) {  // an empty part: O_s = 0, LSE_s = -inf
@@ -418,7 +423,7 @@ void fwd16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K
   // With a ragged last tile, the copy of its rows past the end may leave old
   // LDS contents in place; starting from zeros keeps every value read finite
   // (those keys are masked, so their values only ever meet P = 0).
-  if (N % kBc != 0) {
+  if (Nk % kBc != 0) {
     const u32x4 z = {0, 0, 0, 0};
     for (int i = tid; i < G::kKT / 16; i += kThreads) {
       ((u32x4*)k0s)[i] = z;
@@ -432,10 +437,10 @@ void fwd16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K
   }
 
   auto issue_k = [&](int kt, unsigned char* dst) {
-    copy_tile<D, G::kKPW>(kg + (long long)(kt * kBc) * ksb, N - kt * kBc, ksb, dst, koff, wave);
+    copy_tile<D, G::kKPW>(kg + (long long)(kt * kBc) * ksb, Nk - kt * kBc, ksb, dst, koff, wave);
   };
   auto issue_v = [&](int kt, unsigned char* dst) {
-    copy_tile<D, G::kVPW>(vg + (long long)(kt * kBc) * vsb, N - kt * kBc, vsb, dst, voff, wave);
+    copy_tile<D, G::kVPW>(vg + (long long)(kt * kBc) * vsb, Nk - kt * kBc, vsb, dst, voff, wave);
   };
 
   // Per-lane LDS read bases. K: MFMA row n holds key sigma(n) (second tile:
@@ -495,13 +500,13 @@ void fwd16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K
     }
   };
 
-  // Sets the scores of keys a row may not see (outside qrow - wl ..
-  // qrow + wr, or past the end of the sequence) to -inf. Register r of sc0
+  // Sets the scores of keys a row may not see (outside qpos - wl ..
+  // qpos + wr, or past the end of the keys) to -inf. Register r of sc0
   // holds key kbase + 8*hh + kc(r) with kc(r) = sigma(acc_row(r, 0)); sc1
   // adds 32; a key is visible iff lo <= its kc <= lim.
   auto mask_tile = [&](int kbase) {
-    const int lim = min(qrow + wr, N - 1) - kbase - 8 * hh;
-    const int lo = qrow - wl - kbase - 8 * hh;
+    const int lim = min(qpos + wr, Nk - 1) - kbase - 8 * hh;
+    const int lo = qpos - wl - kbase - 8 * hh;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int kc = 16 * (r >> 3) + 4 * ((r >> 2) & 1) + (r & 3);
@@ -708,8 +713,8 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
                           amdgpu_waves_per_eu(1, 1)))
 void fwd32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
                   const float* __restrict__ V, float* __restrict__ O,
-                  float* __restrict__ LSE, View vq, View vk, View vv, View vo, int H, int N, int nqt,
-                  int nblocks, float c, int wl, int wr, SplitOut sp) {
+                  float* __restrict__ LSE, View vq, View vk, View vv, View vo, int H, int N, int Nk,
+                  int nqt, int nblocks, float c, int wl, int wr, SplitOut sp) {
   constexpr int DCH = D / 4;                  // 16-byte chunks per row
   constexpr int VSTRIDE = D + 8;              // floats per padded V row
   constexpr int KS_BYTES = kBc * D * 4;
@@ -741,6 +746,8 @@ void fwd32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
   const int hh = lane >> 5;
   const int q0 = qt * kBr32 + rb * 32;
   const int qrow = q0 + n;
+  // Positions: query row i sits at i + Nk - N (the last N positions).
+  const int pos_off = Nk - N;
 
   // Q^T operands: k-steps 4u + j use d = 8u + 4hh + j.
   f32x4 qf[D / 8];
@@ -748,11 +755,11 @@ void fwd32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
   for (int u = 0; u < D / 8; ++u)
     qf[u] = qrow < N ? *(const f32x4*)(Q + (long long)qrow * vq.r + 8 * u + 4 * hh) : f32x4{0, 0, 0, 0};
 
-  // Key tiles the block needs (query i sees keys i - wl .. i + wr; wr is 0
-  // when causal, an unbounded side is 2^30).
+  // Key tiles the block needs (a query at position p sees keys p - wl ..
+  // p + wr; wr is 0 when causal, an unbounded side is 2^30).
   const int q_lo = qt * kBr32;
-  int t_lo = max(q_lo - wl, 0) / kBc;
-  int t_end = min(min(q_lo + kBr32 - 1, N - 1) + wr, N - 1) / kBc + 1;
+  int t_lo = max(q_lo + pos_off - wl, 0) / kBc;
+  int t_end = min(min(q_lo + kBr32 - 1, N - 1) + pos_off + wr, Nk - 1) / kBc + 1;
   if (sp.part) {  // an empty part runs no iteration and stores O_s = 0, LSE_s = -inf
     int nkt = t_end - t_lo;
     split_range(blockIdx.y, sp.nsplit, t_lo, nkt);
@@ -767,7 +774,7 @@ void fwd32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
     for (int i = 0; i < CH; ++i) {
       const int g = tid + i * kThreads;
       const int key = g / DCH, ch = g % DCH;
-      const bool ok = k0 + key < N;
+      const bool ok = k0 + key < Nk;
       kreg[i] = ok ? *(const f32x4*)(K + (long long)(k0 + key) * vk.r + ch * 4) : f32x4{0, 0, 0, 0};
       vreg[i] = ok ? *(const f32x4*)(V + (long long)(k0 + key) * vv.r + ch * 4) : f32x4{0, 0, 0, 0};
     }
@@ -787,7 +794,7 @@ void fwd32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
     for (int i = 0; i < CH; ++i) {
       const int g = tid + i * kThreads;
       const int key = g / DCH, ch = g % DCH;
-      const bool ok = k0 + key < N;
+      const bool ok = k0 + key < Nk;
       const f32x4 kx = ok ? *(const f32x4*)(K + (long long)(k0 + key) * vk.r + ch * 4) : f32x4{0, 0, 0, 0};
       const f32x4 vx = ok ? *(const f32x4*)(V + (long long)(k0 + key) * vv.r + ch * 4) : f32x4{0, 0, 0, 0};
       *(f32x4*)(ks + key * (D * 4) + ((ch ^ (key & 7)) << 4)) = kx;
@@ -811,7 +818,7 @@ void fwd32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
     // This wave's keys: kb .. kb + 31. A half tile no row of the wave can
     // see is skipped.
     const int kb = kt * kBc + 32 * kh;
-    if (kb < N && kb <= q0 + 31 + wr && kb + 31 >= q0 - wl) {
+    if (kb < Nk && kb <= q0 + pos_off + 31 + wr && kb + 31 >= q0 + pos_off - wl) {
       f32x16 s = {};
       const int krow = 32 * kh + n;
       const unsigned char* kr = ks + krow * (D * 4);
@@ -821,7 +828,7 @@ void fwd32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
 #pragma unroll
         for (int j = 0; j < 4; ++j) s = __builtin_amdgcn_mfma_f32_32x32x2f32(a[j], qf[u][j], s, 0, 0, 0);
       }
-      const float alpha = online_softmax(s, c, kb, qrow, q0, N, wl, wr, hh, m_run, l_run);
+      const float alpha = online_softmax(s, c, kb, qrow + pos_off, q0 + pos_off, Nk, wl, wr, hh, m_run, l_run);
 #pragma unroll
       for (int t = 0; t < D / 32; ++t) acc[t] *= alpha;
 #pragma unroll
