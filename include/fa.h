@@ -204,9 +204,12 @@ int fa_fwd_kv(const void* q, const void* k, const void* v, void* o, float* lse,
 /*
  * fa_fwd_num_splits - host-only: the number of parts fa_fwd_splitkv uses
  * for num_splits = 0: 1 when the plain grid already fills half the GPU;
- * otherwise enough parts to fill it, at most 16, while each part of the
- * widest query tile keeps at least 16 key tiles (causal) or 32 (not
- * causal). Writes it to *num_splits; returns the shape checks' status.
+ * otherwise, while each part of the widest query tile keeps at least 16 key
+ * tiles (causal) or 32 (not causal): enough parts to fill the GPU's
+ * resident workgroup slots (at most 16), or, with fewer query rows than
+ * half a query tile (a decode step, bound by streaming K and V), about one
+ * workgroup per compute unit (at most 64). Writes it to *num_splits;
+ * returns the shape checks' status.
  *
  * fa_fwd_splitkv_workspace - host-only: the workspace bytes fa_fwd_splitkv
  * needs for num_splits parts (0 for num_splits = 1): 4 * S * B * H * N *

@@ -314,7 +314,12 @@ def test_fwd_kv_checks(N, Nk, causal, left, right, code):
 
 
 def test_fwd_kv_num_splits_for_decode():
-    # one query per head against a long cache: the key range is spread out
-    assert fa.splitkv_num_splits(1, 32, 1, 128, True, Nk=32768) == 16
+    # one query per head against a long cache: about one workgroup per
+    # compute unit (256), at most 64 parts, at least 16 key tiles per part
+    assert fa.splitkv_num_splits(1, 32, 1, 128, True, Nk=32768) == 8
+    assert fa.splitkv_num_splits(1, 4, 1, 128, True, Nk=262144) == 64
+    assert fa.splitkv_num_splits(8, 32, 1, 128, True, Nk=4096) == 1
     assert fa.splitkv_num_splits(1, 32, 1, 128, True, Nk=256) == 1
     assert fa.splitkv_num_splits(4, 64, 2048, 128, True, Nk=4096) == 1
+    # matrix-core bound shapes keep filling the resident slots (at most 16)
+    assert fa.splitkv_num_splits(1, 1, 16384, 128, True) == 4

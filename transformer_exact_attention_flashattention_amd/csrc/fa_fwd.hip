@@ -168,18 +168,24 @@ int resident_blocks(int d, int dtype) { return (dtype == FA_F32 || d == 256) ? 2
 constexpr int kMinTilesCausal = 16;
 constexpr int kMinTiles = 32;
 
-// Parts for a grid of nblocks workgroups: none while the grid fills half
-// the chip; otherwise enough to fill it, as long as each part of the widest
-// query tile keeps the minimum number of key tiles; at most 16.
-int choose_splits(long long nblocks, int Nk, int d, int causal, int wl, int wr, int dtype) {
+// Parts for a grid of nblocks workgroups of N query rows against Nk keys:
+// none while the grid fills half the chip; otherwise, as long as each part
+// of the widest query tile keeps the minimum number of key tiles:
+//  * N of at least half a query tile (the work is matrix-core bound):
+//    enough parts to fill every resident slot, at most 16;
+//  * fewer rows (a decode step: streaming K and V from HBM sets the time):
+//    about one workgroup per compute unit, at most 64.
+// Both targets come from sweeps on one GPU (d = 64 .. 256).
+int choose_splits(long long nblocks, int N, int Nk, int d, int causal, int wl, int wr, int dtype) {
   const int slots = resident_blocks(d, dtype);
   if (nblocks * 2 > slots) return 1;
   long long span = (long long)rows_per_block(dtype) + (wl < 0 ? Nk : wl) + (causal || wr == 0 ? 0 : (wr < 0 ? Nk : wr));
   span = std::min<long long>(span, Nk);
   const int tiles = (int)((span + fa::kBc - 1) / fa::kBc);
-  int s = (int)(slots / std::max<long long>(nblocks, 1));
+  const bool decode = N <= rows_per_block(dtype) / 2;
+  int s = (int)((decode ? 256 : slots) / std::max<long long>(nblocks, 1));
   s = std::min(s, tiles / (causal ? kMinTilesCausal : kMinTiles));
-  s = std::min(s, 16);
+  s = std::min(s, decode ? kMaxSplits : 16);
   return std::max(s, 1);
 }
 
@@ -254,7 +260,7 @@ int fwd_general(const void* q, const void* k, const void* v, void* o, float* lse
   int st =
       plan_fwd(q, k, v, o, lse, strides, B, H, N, Nk, d, scale, causal, window_left, window_right, dtype, &plan);
   if (st != FA_OK || plan.nblocks == 0) return st;
-  int ns = num_splits == 0 ? choose_splits(plan.nblocks, Nk, d, causal, window_left, window_right, dtype)
+  int ns = num_splits == 0 ? choose_splits(plan.nblocks, N, Nk, d, causal, window_left, window_right, dtype)
                            : num_splits;
   float* part = nullptr;
   if (ns > 1) {
@@ -306,7 +312,8 @@ extern "C" int fa_fwd_kv_num_splits(int B, int H, int N, int Nk, int d, int caus
   if (Nk < 0 || Nk > (1 << 30) - fa::kBr) return FA_ERR_SHAPE;
   if (window_left < -1 || window_right < -1) return FA_ERR_ARG;
   if (!num_splits) return FA_ERR_NULL;
-  *num_splits = nblocks == 0 || Nk == 0 ? 1 : choose_splits(nblocks, Nk, d, causal, window_left, window_right, dtype);
+  *num_splits =
+      nblocks == 0 || Nk == 0 ? 1 : choose_splits(nblocks, N, Nk, d, causal, window_left, window_right, dtype);
   return FA_OK;
 }
 
