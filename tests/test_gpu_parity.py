@@ -214,6 +214,29 @@ def test_constant_values():
         assert torch.equal(o, v)
 
 
+def test_grid_remap_does_not_change_results():
+    """With a grid that is a multiple of 8 the workgroup -> (head, tile) map
+    is permuted across XCDs; with 7 heads it is the identity. Heads 0..6
+    come out bitwise the same either way."""
+    q, k, v = inputs.make_qkv(1, 8, 1024, 128, "bf16", seed=16)
+    o8, l8 = run(q, k, v, 0.088, True)       # 8 heads x 8 tiles = 64 workgroups (remapped)
+    o7, l7 = run(q[:, :7].contiguous(), k[:, :7].contiguous(), v[:, :7].contiguous(), 0.088, True)  # 56: identity
+    assert torch.equal(o8[:, :7], o7) and torch.equal(l8[:, :7], l7)
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16", "f32"])
+@pytest.mark.parametrize("D", [64, 128, 256])
+def test_length_4097_sampled_rows(dtype, D):
+    """N = 4097: one row past a power of two, so the last query tile and the
+    last key tile hold a single row."""
+    q, k, v = inputs.make_qkv(1, 1, 4097, D, dtype, seed=D + 4097)
+    rows = np.unique(np.concatenate([np.arange(64), np.arange(4000, 4097), [1023, 1024, 2048]]))
+    for causal in (False, True):
+        o, lse = run(q, k, v, 1.0 / math.sqrt(D), causal)
+        check(o, lse, q, k, v, 1.0 / math.sqrt(D), causal, rows=rows)
+        assert torch.isfinite(o).all() and torch.isfinite(lse).all()
+
+
 def test_deterministic_bitwise():
     q, k, v = inputs.make_qkv(1, 8, 1500, 128, "bf16", seed=13)
     outs = [run(q, k, v, 0.088, True) for _ in range(3)]

@@ -312,10 +312,18 @@ __device__ __forceinline__ void copy_tile(const unsigned char* src, int nvalid, 
 }
 
 // s_waitcnt vmcnt(X) for a compile-time X (lgkmcnt and expcnt not waited on).
+// The race-check build (FA_SYNC_CHECK, libfa_sync.so) waits for every copy
+// instead, and its tile_barrier below is a full __syncthreads(): with no
+// copy in flight across any barrier, a missing wait in the normal build
+// would show as a difference between the two builds' results.
 template <int X>
 __device__ __forceinline__ void wait_vmcnt() {
   static_assert(X >= 0 && X < 64, "vmcnt is 6 bits");
+#if defined(FA_SYNC_CHECK)
+  __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));  // vmcnt(0)
+#else
   __builtin_amdgcn_s_waitcnt((X & 15) | ((X >> 4) << 14) | (7 << 4) | (15 << 8));
+#endif
 }
 
 // Workgroup barrier for the key loop. __syncthreads() is a release/acquire
@@ -327,10 +335,15 @@ __device__ __forceinline__ void wait_vmcnt() {
 // (wait_vmcnt) for the copies whose data the next phase reads. The empty
 // asm statements keep the compiler from moving memory accesses across it.
 __device__ __forceinline__ void tile_barrier() {
+#if defined(FA_SYNC_CHECK)
+  __builtin_amdgcn_s_waitcnt(0);  // every counter
+  __syncthreads();
+#else
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0) only
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
+#endif
 }
 
 // Scheduling masks of __builtin_amdgcn_sched_group_barrier.
