@@ -575,6 +575,10 @@ void fwd16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K
   s_tile(k0s, std::integral_constant<int, 0>{});
   __builtin_amdgcn_sched_barrier(0);
   if (!is_full(t_lo)) mask_tile(t_lo * kBc);
+  // The first tile's own max is the first exponent reference, so its P need
+  // not be computed twice (a row with no visible key in it keeps -inf and
+  // takes the move in the first iteration, as every row did before).
+  m_run = tile_max();
 
   constexpr int kNK = G::kKPW, kNV = G::kVPW;  // copies per wave per tile
 
