@@ -1,7 +1,9 @@
-// fa_kernels.h - gfx950 kernels for the exact-attention forward pass.
+// fa_kernels.h - gfx950 kernels for the exact-attention forward pass (and
+// the split-KV merge), plus the helpers the backward kernels share.
 //
 // What is computed (per batch b, head h, query row i):
-//   S_ij = scale * q_i . k_j, masked to -inf for j > i when causal,
+//   S_ij = scale * q_i . k_j, masked to -inf for j > i when causal (and
+//          outside a local window),
 //   O_i  = sum_j softmax(S_i)_j v_j,  LSE_i = ln sum_j exp(S_ij),
 // the standard three-step attention of section 1.1 of "2.3 FlashAttention
 // and IO-aware attention" (aiknowledge.cn), evaluated blockwise with the
@@ -32,7 +34,12 @@
 //    from its natural layout by ds_read_b64_tr_b16 (fp32 tiles go through
 //    registers);
 //  * causal: key tiles past the workgroup's last row are never loaded, and
-//    only diagonal or ragged tiles pay for the element mask.
+//    only diagonal or ragged tiles pay for the element mask; a window
+//    narrows the tile range the same way from both sides;
+//  * operands are strided views (View), so packed tensors are read in place;
+//    with fewer queries than keys the queries take the last positions;
+//  * split-KV runs the same kernels on a 2-D grid (query tile x key part)
+//    and merge_kernel combines the parts' results by log-sum-exp.
 #pragma once
 
 #include <hip/hip_runtime.h>
