@@ -43,11 +43,19 @@ def metric_flops(c):
 
 
 def kernel_source_digest():
+    """SHA-256 of the forward kernel sources with comments and blank space
+    removed, so that an edit of a comment does not void measured counters."""
+    import re
+
     h = hashlib.sha256()
     for rel in ("transformer_exact_attention_flashattention_amd/csrc/fa_kernels.h",
                 "transformer_exact_attention_flashattention_amd/csrc/fa_fwd.hip"):
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, rel), encoding="utf-8") as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", "", text)
+        text = "\n".join(line.strip() for line in text.splitlines() if line.strip())
+        h.update(text.encode())
     return h.hexdigest()
 
 
