@@ -1,0 +1,102 @@
+"""Randomised GPU parity: 48 forward cases drawn with a fixed seed over every
+option at once (dtype, head dim, batch, heads, query and key lengths,
+causal, window, split-KV parts, strided operands), each against the fp64
+oracle with the bounds of test_gpu_parity.py, and 16 backward cases against
+the gradient oracle with the bounds of test_gpu_bwd.py. The draw is printed
+with each case, so a failure names its configuration."""
+
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import transformer_exact_attention_flashattention_amd as fa
+from transformer_exact_attention_flashattention_amd import build as fabuild
+from transformer_exact_attention_flashattention_amd import inputs
+from oracle import attention_bwd_ref, attention_ref
+
+pytestmark = pytest.mark.gpu
+
+DT = {"f16": torch.float16, "bf16": torch.bfloat16, "f32": torch.float32}
+TOL_O = {"f16": 2e-3, "bf16": 1e-2, "f32": 1e-5}
+TOL_LSE = 1e-3
+TOL_G = {"f16": 2e-3, "bf16": 1e-2}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu_ready():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+    if not fabuild.is_built():
+        fabuild.build()
+    fa.lib()
+
+
+def draw_forward(i):
+    rng = np.random.default_rng(1000 + i)
+    dtype = str(rng.choice(["f16", "bf16", "f32"]))
+    D = int(rng.choice([64, 128, 256]))
+    B, H = int(rng.integers(1, 3)), int(rng.integers(1, 4))
+    N = int(rng.choice([1, 17, 64, 130, 257, 700]))
+    Nk = N if rng.random() < 0.6 else N + int(rng.integers(0, 900))
+    causal = bool(rng.random() < 0.5)
+    window = (-1, -1)
+    if rng.random() < 0.35:
+        window = (int(rng.choice([-1, 0, 5, 80, 300])), int(rng.choice([-1, 0, 7, 120])))
+    splits = int(rng.choice([1, 1, 0, 2, 5]))
+    layout = str(rng.choice(["bhnd", "bnhd"]))
+    return dict(dtype=dtype, D=D, B=B, H=H, N=N, Nk=Nk, causal=causal, window=window, splits=splits,
+                layout=layout)
+
+
+@pytest.mark.parametrize("i", range(48))
+def test_forward_fuzz(i):
+    c = draw_forward(i)
+    sys.__stderr__.write(f"\n[gpu case] forward fuzz {i}: {c}\n")
+    sys.__stderr__.flush()
+    q = inputs.make_qkv(c["B"], c["H"], c["N"], c["D"], c["dtype"], seed=i)[0]
+    _, k, v = inputs.make_qkv(c["B"], c["H"], c["Nk"], c["D"], c["dtype"], seed=i + 500)
+    if c["layout"] == "bnhd":  # [B, N, H, d] storage, passed as transposed views
+        qd, kd, vd = (t.transpose(1, 2).contiguous().cuda().transpose(1, 2) for t in (q, k, v))
+    else:
+        qd, kd, vd = (t.cuda() for t in (q, k, v))
+    o = torch.full(q.shape, float("nan"), dtype=q.dtype, device="cuda")
+    lse = torch.full(q.shape[:3], float("nan"), device="cuda")
+    fa.fwd(qd, kd, vd, causal=c["causal"], window_size=c["window"], out=o, lse=lse, num_splits=c["splits"])
+    torch.cuda.synchronize()
+    scale = 1.0 / math.sqrt(c["D"])
+    o_ref, l_ref = attention_ref(q.double().numpy(), k.double().numpy(), v.double().numpy(), scale, c["causal"],
+                                 window=c["window"])
+    o64, l64 = o.double().cpu().numpy(), lse.double().cpu().numpy()
+    assert np.isfinite(o64).all() and np.isfinite(l64).all()
+    assert np.abs(o64 - o_ref).max() <= TOL_O[c["dtype"]]
+    assert np.abs(l64 - l_ref).max() <= TOL_LSE
+
+
+def draw_backward(i):
+    rng = np.random.default_rng(2000 + i)
+    return dict(dtype=str(rng.choice(["f16", "bf16"])), D=int(rng.choice([64, 128, 256])),
+                B=int(rng.integers(1, 3)), H=int(rng.integers(1, 3)), N=int(rng.choice([1, 33, 128, 200, 513])),
+                causal=bool(rng.random() < 0.5),
+                window=(-1, -1) if rng.random() < 0.6 else (int(rng.choice([0, 9, 100])), int(rng.choice([-1, 4]))))
+
+
+@pytest.mark.parametrize("i", range(16))
+def test_backward_fuzz(i):
+    c = draw_backward(i)
+    sys.__stderr__.write(f"\n[gpu case] backward fuzz {i}: {c}\n")
+    sys.__stderr__.flush()
+    q, k, v = inputs.make_qkv(c["B"], c["H"], c["N"], c["D"], c["dtype"], seed=i + 3000)
+    do = torch.randn(q.shape, generator=torch.Generator().manual_seed(i)).to(q.dtype)
+    qd, kd, vd, dod = (t.cuda() for t in (q, k, v, do))
+    o, lse = fa.fwd(qd, kd, vd, causal=c["causal"], window_size=c["window"])
+    grads = fa.bwd(qd, kd, vd, o, lse, dod, causal=c["causal"], window_size=c["window"])
+    torch.cuda.synchronize()
+    ref = attention_bwd_ref(q.double().numpy(), k.double().numpy(), v.double().numpy(), do.double().numpy(),
+                            1.0 / math.sqrt(c["D"]), c["causal"], c["window"])
+    for got, r in zip(grads, ref):
+        g = got.double().cpu().numpy()
+        assert np.isfinite(g).all()
+        assert np.abs(g - r).max() / max(np.abs(r).max(), 1.0) <= TOL_G[c["dtype"]]
