@@ -243,7 +243,7 @@ void dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   __shared__ __attribute__((aligned(1024))) unsigned char st1[2 * TB];
 
   int bh, qt;
-  decode_block(nblocks, nqt, CAUSAL, bh, qt);
+  decode_block(nblocks, nqt, CAUSAL, bh, qt, D >= 256 ? 32 : 64);
   Q += view_base(vq, bh, H);
   K += view_base(vk, bh, H);
   V += view_base(vv, bh, H);
@@ -412,10 +412,12 @@ void dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   __shared__ __attribute__((aligned(1024))) unsigned char st1[SB];
   __shared__ __attribute__((aligned(1024))) unsigned char st2[SB];
 
-  // Key blocks in order: with a causal mask the first blocks have the most
-  // query tiles, so they start first.
+  // With a causal mask the first key blocks have the most query tiles, so
+  // they start first: decode_block's longest-first order (which counts
+  // query tiles from the last) read backwards.
   int bh, kb;
-  decode_block(nblocks, nkb, false, bh, kb);
+  decode_block(nblocks, nkb, CAUSAL, bh, kb);
+  if (CAUSAL) kb = nkb - 1 - kb;
   Q += view_base(vq, bh, H);
   K += view_base(vk, bh, H);
   V += view_base(vv, bh, H);
