@@ -485,13 +485,17 @@ void dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const unsigned char* const gs = st + TB;
     const float* const ls = (const float*)(st + 2 * TB);
     const float* const dls = ls + kStatSlots;
-    // This step's copies landed (those of the next step may still fly),
-    // then every wave's copies are visible.
-    if (qt + 1 <= qt_hi) wait_vmcnt<kCopies>();
-    else wait_vmcnt<0>();
+    // This step's copies landed (those issued one step later may still
+    // fly), then every wave's copies are visible.
+    wait_vmcnt<kCopies>();
     tile_barrier();
     // The stage of step qt - 1 is free now: refill it with step qt + 2.
-    if (qt + 2 <= qt_hi) issue(qt + 2, st_next);
+    // Past the last step the copy repeats the last step's tile, so every
+    // step issues the same copies and waits for the same count. (With a
+    // conditional copy the compiler cannot tell, at the third stage's
+    // reads, whether that stage's copies are the newest in flight, and
+    // drains every copy there.)
+    issue(min(qt + 2, qt_hi), st_next);
     const int qbase = qt * kQT;
     // Skip the step if no query of it sees a key of the wave; take the
     // unmasked path if every query of it sees every key of the wave.
@@ -594,7 +598,7 @@ void dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   // Prologue: the first two steps in flight; then three steps per turn of
   // the ring (stage of step qt: (qt - qt_lo) % 3).
   issue(qt_lo, st0);
-  if (qt_lo + 1 <= qt_hi) issue(qt_lo + 1, st1);
+  issue(min(qt_lo + 1, qt_hi), st1);
   int qt = qt_lo;
   for (; qt + 2 <= qt_hi; qt += 3) {
     step(qt, st0, st2);
@@ -603,6 +607,8 @@ void dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   }
   if (qt <= qt_hi) step(qt, st0, st2);
   if (qt + 1 <= qt_hi) step(qt + 1, st1, st0);
+  // The repeated copies of the last steps land before the wave ends.
+  wait_vmcnt<0>();
 
   if (krow < N) {
     uint16_t* krow_k = dK + (long long)krow * vdk.r;
