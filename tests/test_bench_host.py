@@ -1,0 +1,78 @@
+"""Host logic of bench.py (no GPU): the one-GPU guard, the metric's flop
+count, and the rule that ties roofline.traffic to the kernel sources the
+counters were taken on."""
+
+import importlib.util
+import json
+import os
+import shutil
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SOURCES = ("transformer_exact_attention_flashattention_amd/csrc/fa_kernels.h",
+           "transformer_exact_attention_flashattention_amd/csrc/fa_fwd.hip")
+
+
+@pytest.fixture(scope="module")
+def bench():
+    spec = importlib.util.spec_from_file_location("bench_under_test", os.path.join(ROOT, "bench.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+    assert r.stdout == ""  # no JSON line for a run that did not happen
+
+
+def test_metric_flops(bench):
+    c = {"B": 1, "H": 16, "N": 16384, "D": 256, "causal": True}
+    assert bench.metric_flops(c) == 4.0 * 16 * 16384 ** 2 * 256 / 2
+    c["causal"] = False
+    assert bench.metric_flops(c) == 4.0 * 16 * 16384 ** 2 * 256
+
+
+def copy_sources(dst):
+    for rel in SOURCES:
+        os.makedirs(os.path.join(dst, os.path.dirname(rel)), exist_ok=True)
+        shutil.copy(os.path.join(ROOT, rel), os.path.join(dst, rel))
+
+
+def test_digest_ignores_comments_but_not_code(bench, tmp_path, monkeypatch):
+    copy_sources(tmp_path)
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    d0 = bench.kernel_source_digest()
+    hip = tmp_path / SOURCES[1]
+    text = hip.read_text()
+    hip.write_text("// a new comment line\n\n" + text.replace("\n", "  /* trailing */\n", 1))
+    assert bench.kernel_source_digest() == d0
+    hip.write_text(text.replace("constexpr int kMaxSplits = 64;", "constexpr int kMaxSplits = 63;"))
+    assert bench.kernel_source_digest() != d0
+
+
+def test_traffic_only_for_matching_sources(bench, tmp_path, monkeypatch):
+    good = {"kernel_sha256": bench.kernel_source_digest(), "hbm_bytes_per_launch": 1.25e9}
+    f = tmp_path / "traffic.json"
+    f.write_text(json.dumps(good))
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(f))
+    assert bench.load_traffic(0) == 1.25e9
+    f.write_text(json.dumps(dict(good, kernel_sha256="0" * 64)))
+    assert bench.load_traffic(0) is None
+    f.write_text("not json")
+    assert bench.load_traffic(0) is None
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(tmp_path / "missing.json"))
+    assert bench.load_traffic(0) is None
+
+
+def test_committed_traffic_file_is_well_formed(bench):
+    with open(bench.TRAFFIC_FILE) as f:
+        t = json.load(f)
+    assert len(t["kernel_sha256"]) == 64
+    assert t["hbm_bytes_per_launch"] > 0
