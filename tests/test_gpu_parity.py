@@ -153,6 +153,33 @@ def test_other_scales(scale):
         check(o, lse, q, k, v, scale, causal, tol_o=tol)
 
 
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("D", [64, 128, 256])
+def test_reference_moves_on_growing_logits(dtype, D):
+    """Key norms that grow along the sequence (x0.05 .. x4) at twice the
+    default scale make later key tiles' scores exceed the first tile's
+    maximum by far more than 8 in exp2 units, the point at which the 16-bit
+    kernel moves its exponent reference and rescales the output it has
+    accumulated so far: many rows take that rare path, in tiles after
+    the first. V is scaled by 1/4, so |O| stays below about 1 and the usual
+    bound applies to the peaky softmax this gives."""
+    N = 700
+    q, k, v = inputs.make_qkv(1, 2, N, D, dtype, seed=21)
+    ramp = torch.linspace(0.05, 4.0, N).view(1, 1, N, 1)
+    k = (k.float() * ramp).to(k.dtype)
+    v = (v.float() * 0.25).to(v.dtype)
+    scale = 2.0 / math.sqrt(D)
+    # The inputs do force moves: per row, the scores' maximum over all keys
+    # minus their maximum over the first 64 keys, in exp2 units.
+    s2 = np64(q)[0, 0] @ np64(k)[0, 0].T * scale * math.log2(math.e)
+    assert ((s2.max(axis=1) - s2[:, :64].max(axis=1)) > 8).mean() > 0.9
+    for causal in (False, True):
+        o, lse = run(q, k, v, scale, causal)
+        check(o, lse, q, k, v, scale, causal)
+    o, lse = run(q, k, v, scale, True, window=(300, -1))
+    check(o, lse, q, k, v, scale, True, window=(300, -1))
+
+
 # ----------------------------------------------------- GPU-side invariants --
 
 @pytest.mark.parametrize("dtype", ["f16", "bf16", "f32"])
