@@ -452,7 +452,7 @@ def bench_sweep(fa, inputs, dev, stream, no_parity):
                     err_o, err_l = check_parity(o[:, :1].cpu(), lse[:, :1].cpu(), q[:, :1], k[:, :1], v[:, :1], scale,
                                                 causal, rows)
                     ok = err_o <= 1e-2 and err_l <= 1e-3
-                _, per = time_launches(step, stream, 10, 5, settle_ms=200.0)
+                _, per = time_launches(step, stream, 10, 5, settle_ms=600.0)
                 ms = float(np.mean(per))
                 fl = 4.0 * H * N * N * D / (2 if causal else 1)
                 res.append({"N": N, "H": H, "d": D, "causal": causal, "kernel_ms_mean": round(ms, 4),
