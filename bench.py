@@ -96,7 +96,7 @@ def gpu_settle(ms):
         torch.cuda.synchronize()
 
 
-def time_launches(fn, stream, steps, warmup, settle_ms=400.0):
+def time_launches(fn, stream, steps, warmup, settle_ms=600.0):
     """Per-launch kernel times (ms, sorted) from an event pair around each
     call: `warmup` untimed calls, then `steps` timed ones. settle_ms > 0
     first runs gpu_settle for that long."""
@@ -505,7 +505,7 @@ def main():
                           "data": "synthetic: i.i.d. N(0,1) Q, K, V cast to bf16"}), flush=True)
         sys.exit(1 if any(r["parity_ok"] is False for r in sweep) else 0)
 
-    def run_config(cfg, steps, warmup, check_rows, window=(-1, -1), settle_ms=400.0):
+    def run_config(cfg, steps, warmup, check_rows, window=(-1, -1), settle_ms=600.0):
         c = inputs.CONFIGS[cfg]
         log(f"[bench] config {cfg} ({c['name']}): generating inputs")
         q, k, v = inputs.make_config(cfg)
