@@ -20,10 +20,11 @@
 //    owns one query), then dQ^T += K^T dS^T with K^T read transposed from
 //    LDS and dS^T as the B operand;
 //  * dkdv_kernel: one workgroup per (batch*head, 128-key block), each wave
-//    owning 32 keys with K^T and V^T held as B operands; per 32-query step,
-//    S = Q K^T and dP = dO V^T with Q and dO from LDS, P and dS per lane
-//    (each lane owns one key), then dV^T += dO^T P and dK^T += Q^T dS with
-//    dO^T and Q^T read transposed from LDS.
+//    owning 32 keys with K^T and V^T held as B operands (at d = 256 V^T is
+//    read from an LDS copy of the block's V rows instead); per 32-query
+//    step, S = Q K^T and dP = dO V^T with Q and dO from LDS, P and dS per
+//    lane (each lane owns one key), then dV^T += dO^T P and dK^T += Q^T dS
+//    with dO^T and Q^T read transposed from LDS.
 // The index tricks are the forward's: rows of an A operand are read through
 // the permutation sigma, which makes the accumulator of one product the B
 // operand layout of the next.
@@ -390,11 +391,12 @@ constexpr int kStatSlots = 64;  // LDS floats reserved for LSE (and for delta) p
 // 192 registers per lane at d = 128. Query tiles (Q, dO, LSE, delta) stream
 // through a ring of three LDS stages filled by direct copies issued two
 // steps ahead.
-// PART selects the gradients: 0 both, 1 dV only, 2 dK only. At d = 256 the
-// two accumulators and the K^T, V^T operands do not fit the registers
-// together, so the host runs the kernel twice (1, then 2), each pass
-// recomputing S (and the dK pass dP) for its own gradient.
-template <class T, int D, bool CAUSAL, int PART>
+// VL (d = 256): V^T is read from an LDS copy of the block's V rows instead
+// of registers. At d = 256 the two accumulators and the K^T, V^T operands
+// do not fit the registers together (held all in registers, the kernel
+// spilled); the V copy (64 KiB plus padding) leaves LDS room for a ring of
+// two stages only, refilled one step ahead.
+template <class T, int D, bool CAUSAL, bool VL>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(1, 1)))
 void dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                  const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
@@ -404,13 +406,18 @@ void dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   // One array per stage: Q tile, dO tile, LSE (natural log), delta. (Few
   // distinct arrays, so that the compiler can still tell the copies into
   // one stage from the reads of another and does not wait on them.)
-  constexpr bool kV = PART != 2, kK = PART != 1;
+  constexpr bool kVL = VL;  // V^T operands from the LDS copy
+  constexpr int kStages = kVL ? 2 : 3;
   constexpr int kQT = dkdv_step_rows<D>();
   constexpr int TB = kQT * Tile<D>::kRS;
   constexpr int SB = 2 * TB + 2 * kStatSlots * 4;
   __shared__ __attribute__((aligned(1024))) unsigned char st0[SB];
   __shared__ __attribute__((aligned(1024))) unsigned char st1[SB];
-  __shared__ __attribute__((aligned(1024))) unsigned char st2[SB];
+  __shared__ __attribute__((aligned(1024))) unsigned char st2[kStages == 3 ? SB : 16];
+  // The block's 128 V rows, rows 2d + 16 bytes apart (the 16 rows read by a
+  // 16-lane phase then hit distinct banks).
+  constexpr int kVS = 2 * D + 16;
+  __shared__ __attribute__((aligned(1024))) unsigned char vblk[kVL ? kBr * kVS : 16];
 
   // With a causal mask the first key blocks have the most query tiles, so
   // they start first: decode_block's longest-first order (which counts
@@ -442,13 +449,30 @@ void dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
 
   // K^T and V^T as B operands: lane (n, hh), k-step s holds row krow,
   // columns 16s + 8hh .. +7.
-  u32x4 kf[D / 16], vf[D / 16];
+  u32x4 kf[D / 16], vf[kVL ? 1 : D / 16];
 #pragma unroll
   for (int s = 0; s < D / 16; ++s) {
     kf[s] = krow < N ? *(const u32x4*)(K + (long long)krow * vk.r + 16 * s + 8 * hh) : u32x4{0, 0, 0, 0};
-    if constexpr (kK)
+    if constexpr (!kVL)
       vf[s] = krow < N ? *(const u32x4*)(V + (long long)krow * vv.r + 16 * s + 8 * hh) : u32x4{0, 0, 0, 0};
   }
+  if constexpr (kVL) {
+    // V rows of the block into LDS (zeros past N); the first step's barrier
+    // makes them visible.
+    for (int i = tid; i < kBr * (D / 8); i += kThreads) {
+      const int r = i / (D / 8), ch = i - r * (D / 8);
+      const int key = kb * kBr + r;
+      const u32x4 x = key < N ? *(const u32x4*)(V + (long long)key * vv.r + 8 * ch) : u32x4{0, 0, 0, 0};
+      *(u32x4*)(vblk + r * kVS + 16 * ch) = x;
+    }
+  }
+  // V^T B operand of k-step s (row krow, columns 16s + 8hh .. +7).
+  auto vop = [&](int s) {
+    if constexpr (kVL)
+      return *(const u32x4*)(vblk + (32 * wave + n) * kVS + 32 * s + 16 * hh);
+    else
+      return vf[s];
+  };
 
   // Queries that see a key of the block: i - wl <= j <= i + wr.
   const int k_lo = kb * kBr;
@@ -462,7 +486,7 @@ void dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     for (int i = tid; i < SB / 16; i += kThreads) {
       ((u32x4*)st0)[i] = u32x4{0, 0, 0, 0};
       ((u32x4*)st1)[i] = u32x4{0, 0, 0, 0};
-      ((u32x4*)st2)[i] = u32x4{0, 0, 0, 0};
+      if constexpr (kStages == 3) ((u32x4*)st2)[i] = u32x4{0, 0, 0, 0};
     }
     __syncthreads();
   }
@@ -485,17 +509,25 @@ void dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const unsigned char* const gs = st + TB;
     const float* const ls = (const float*)(st + 2 * TB);
     const float* const dls = ls + kStatSlots;
-    // This step's copies landed (those issued one step later may still
-    // fly), then every wave's copies are visible.
-    wait_vmcnt<kCopies>();
-    tile_barrier();
-    // The stage of step qt - 1 is free now: refill it with step qt + 2.
-    // Past the last step the copy repeats the last step's tile, so every
-    // step issues the same copies and waits for the same count. (With a
-    // conditional copy the compiler cannot tell, at the third stage's
-    // reads, whether that stage's copies are the newest in flight, and
-    // drains every copy there.)
-    issue(min(qt + 2, qt_hi), st_next);
+    if constexpr (kStages == 3) {
+      // This step's copies landed (those issued one step later may still
+      // fly), then every wave's copies are visible.
+      wait_vmcnt<kCopies>();
+      tile_barrier();
+      // The stage of step qt - 1 is free now: refill it with step qt + 2.
+      // Past the last step the copy repeats the last step's tile, so every
+      // step issues the same copies and waits for the same count. (With a
+      // conditional copy the compiler cannot tell, at the third stage's
+      // reads, whether that stage's copies are the newest in flight, and
+      // drains every copy there.)
+      issue(min(qt + 2, qt_hi), st_next);
+    } else {
+      // Two stages: this step's copies are the only ones in flight; after
+      // the barrier the other stage (step qt - 1) takes step qt + 1.
+      wait_vmcnt<0>();
+      tile_barrier();
+      issue(min(qt + 1, qt_hi), st_next);
+    }
     const int qbase = qt * kQT;
     // Skip the step if no query of it sees a key of the wave; take the
     // unmasked path if every query of it sees every key of the wave.
@@ -512,7 +544,7 @@ void dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
 #pragma unroll
       for (int s = 0; s < D / 16; ++s) {
         sa = T::mfma(op.row(qs, 32 * qh, s), kf[s], sa);
-        if constexpr (kK) ga = T::mfma(op.row(gs, 32 * qh, s), vf[s], ga);
+        ga = T::mfma(op.row(gs, 32 * qh, s), vop(s), ga);
       }
       __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 8, 0);
 #pragma unroll
@@ -555,10 +587,10 @@ void dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
             const int r = 8 * cc + 2 * w + e;
             const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sa[r], c, -l2[r]));
             pv[e] = p;
-            if constexpr (kK) dsv[e] = p * (ga[r] - dl[r]);
+            dsv[e] = p * (ga[r] - dl[r]);
           }
-          if constexpr (kV) pp[cc][w] = T::pack(pv[0], pv[1]);
-          if constexpr (kK) dsp[cc][w] = T::pack(dsv[0], dsv[1]);
+          pp[cc][w] = T::pack(pv[0], pv[1]);
+          dsp[cc][w] = T::pack(dsv[0], dsv[1]);
         }
       };
       make_chunk(0);
@@ -568,8 +600,8 @@ void dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
       // k-step's MFMAs.
 #pragma unroll
       for (int tb = 0; tb < D / 32; ++tb) {
-        if constexpr (kV) dv[tb] = T::mfma(op.tr(gs, 2 * qh, tb), pp[0], dv[tb]);
-        if constexpr (kK) dk[tb] = T::mfma(op.tr(qs, 2 * qh, tb), dsp[0], dk[tb]);
+        dv[tb] = T::mfma(op.tr(gs, 2 * qh, tb), pp[0], dv[tb]);
+        dk[tb] = T::mfma(op.tr(qs, 2 * qh, tb), dsp[0], dk[tb]);
       }
       make_chunk(1);
       __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 8, 0);
@@ -582,8 +614,8 @@ void dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int tb = 0; tb < D / 32; ++tb) {
-        if constexpr (kV) dv[tb] = T::mfma(op.tr(gs, 2 * qh + 1, tb), pp[1], dv[tb]);
-        if constexpr (kK) dk[tb] = T::mfma(op.tr(qs, 2 * qh + 1, tb), dsp[1], dk[tb]);
+        dv[tb] = T::mfma(op.tr(gs, 2 * qh + 1, tb), pp[1], dv[tb]);
+        dk[tb] = T::mfma(op.tr(qs, 2 * qh + 1, tb), dsp[1], dk[tb]);
       }
       __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 8, 0);
 #pragma unroll
@@ -596,17 +628,27 @@ void dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   };
 
   // Prologue: the first two steps in flight; then three steps per turn of
-  // the ring (stage of step qt: (qt - qt_lo) % 3).
-  issue(qt_lo, st0);
-  issue(min(qt_lo + 1, qt_hi), st1);
+  // the ring (stage of step qt: (qt - qt_lo) % 3). With two stages: the
+  // first step in flight, then two steps per turn.
   int qt = qt_lo;
-  for (; qt + 2 <= qt_hi; qt += 3) {
-    step(qt, st0, st2);
-    step(qt + 1, st1, st0);
-    step(qt + 2, st2, st1);
+  if constexpr (kStages == 3) {
+    issue(qt_lo, st0);
+    issue(min(qt_lo + 1, qt_hi), st1);
+    for (; qt + 2 <= qt_hi; qt += 3) {
+      step(qt, st0, st2);
+      step(qt + 1, st1, st0);
+      step(qt + 2, st2, st1);
+    }
+    if (qt <= qt_hi) step(qt, st0, st2);
+    if (qt + 1 <= qt_hi) step(qt + 1, st1, st0);
+  } else {
+    issue(qt_lo, st0);
+    for (; qt + 1 <= qt_hi; qt += 2) {
+      step(qt, st0, st1);
+      step(qt + 1, st1, st0);
+    }
+    if (qt <= qt_hi) step(qt, st0, st1);
   }
-  if (qt <= qt_hi) step(qt, st0, st2);
-  if (qt + 1 <= qt_hi) step(qt + 1, st1, st0);
   // The repeated copies of the last steps land before the wave ends.
   wait_vmcnt<0>();
 
@@ -617,18 +659,14 @@ void dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     for (int tb = 0; tb < D / 32; ++tb) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        if constexpr (kK) {
-          u32x2 ok;
-          ok.x = T::pack(dk[tb][4 * g] * scale, dk[tb][4 * g + 1] * scale);
-          ok.y = T::pack(dk[tb][4 * g + 2] * scale, dk[tb][4 * g + 3] * scale);
-          *(u32x2*)(krow_k + 32 * tb + 8 * g + 4 * hh) = ok;
-        }
-        if constexpr (kV) {
-          u32x2 ov;
-          ov.x = T::pack(dv[tb][4 * g], dv[tb][4 * g + 1]);
-          ov.y = T::pack(dv[tb][4 * g + 2], dv[tb][4 * g + 3]);
-          *(u32x2*)(krow_v + 32 * tb + 8 * g + 4 * hh) = ov;
-        }
+        u32x2 ok;
+        ok.x = T::pack(dk[tb][4 * g] * scale, dk[tb][4 * g + 1] * scale);
+        ok.y = T::pack(dk[tb][4 * g + 2] * scale, dk[tb][4 * g + 3] * scale);
+        *(u32x2*)(krow_k + 32 * tb + 8 * g + 4 * hh) = ok;
+        u32x2 ov;
+        ov.x = T::pack(dv[tb][4 * g], dv[tb][4 * g + 1]);
+        ov.y = T::pack(dv[tb][4 * g + 2], dv[tb][4 * g + 3]);
+        *(u32x2*)(krow_v + 32 * tb + 8 * g + 4 * hh) = ov;
       }
     }
   }
@@ -643,22 +681,18 @@ template <class T>
 struct BwdKernels {
   const void* delta;
   const void* dq;
-  const void* dkdv;   // both gradients, or dV only when dk_only is set
-  const void* dk_only;
+  const void* dkdv;
   int rows_per_delta_block;
 };
 
 template <class T, int D>
 BwdKernels<T> pick_d(bool causal) {
-  // d = 256: dV and dK in two passes; otherwise one kernel for both.
-  constexpr int P0 = D >= 256 ? 1 : 0;
-  const void* dk2 = nullptr;
-  if constexpr (D >= 256)
-    dk2 = causal ? (const void*)fa::bwd::dkdv_kernel<T, D, true, 2> : (const void*)fa::bwd::dkdv_kernel<T, D, false, 2>;
+  // d = 256: V^T read from LDS; otherwise K^T and V^T both in registers.
+  constexpr bool VL = D >= 256;
   return {(const void*)fa::bwd::delta_kernel<T, D>,
           causal ? (const void*)fa::bwd::dq_kernel<T, D, true> : (const void*)fa::bwd::dq_kernel<T, D, false>,
-          causal ? (const void*)fa::bwd::dkdv_kernel<T, D, true, P0> : (const void*)fa::bwd::dkdv_kernel<T, D, false, P0>,
-          dk2, fa::kThreads / (D / 8)};
+          causal ? (const void*)fa::bwd::dkdv_kernel<T, D, true, VL> : (const void*)fa::bwd::dkdv_kernel<T, D, false, VL>,
+          fa::kThreads / (D / 8)};
 }
 
 template <class T>
@@ -747,14 +781,13 @@ extern "C" int fa_bwd_strided(const void* q, const void* k, const void* v, const
   const void* kd;
   const void* kq;
   const void* kkv;
-  const void* kk2;
   int rpb;
   if (dtype == FA_BF16) {
     const auto kk = pick<fa::Bf16>(d, causal != 0);
-    kd = kk.delta, kq = kk.dq, kkv = kk.dkdv, kk2 = kk.dk_only, rpb = kk.rows_per_delta_block;
+    kd = kk.delta, kq = kk.dq, kkv = kk.dkdv, rpb = kk.rows_per_delta_block;
   } else {
     const auto kk = pick<fa::F16>(d, causal != 0);
-    kd = kk.delta, kq = kk.dq, kkv = kk.dkdv, kk2 = kk.dk_only, rpb = kk.rows_per_delta_block;
+    kd = kk.delta, kq = kk.dq, kkv = kk.dkdv, rpb = kk.rows_per_delta_block;
   }
   hipStream_t st = (hipStream_t)stream;
 
@@ -788,8 +821,6 @@ extern "C" int fa_bwd_strided(const void* q, const void* k, const void* v, const
                    (void*)&n_arg,   (void*)&nt,      (void*)&nb,      (void*)&c,       (void*)&sc,
                    (void*)&wl,      (void*)&wr};
   if (hipLaunchKernel(kkv, dim3((unsigned)blocks), dim3(fa::kThreads), kargs, 0, st) != hipSuccess)
-    return FA_ERR_LAUNCH;
-  if (kk2 && hipLaunchKernel(kk2, dim3((unsigned)blocks), dim3(fa::kThreads), kargs, 0, st) != hipSuccess)
     return FA_ERR_LAUNCH;
   return FA_OK;
 }
