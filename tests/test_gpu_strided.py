@@ -133,7 +133,7 @@ def grads_contiguous(q, k, v, do, causal, window=(-1, -1)):
 
 
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
-@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("D", [64, 128, 256])
 @pytest.mark.parametrize("causal", [False, True])
 def test_packed_backward(dtype, D, causal):
     """flash_attn_qkvpacked_func's backward writes the packed gradient in
