@@ -248,8 +248,9 @@ int fa_fwd_splitkv_workspace(int B, int H, int N, int d, int num_splits, long lo
  * dtype       FA_F16 or FA_BF16 (fp32 is not supported by the backward).
  *
  * Ownership, synchronisation and errors as fa_fwd: the caller owns every
- * buffer, nothing is allocated, and three kernels are enqueued on stream in
- * order (delta, then dq, then dk/dv); the result does not depend on
+ * buffer, nothing is allocated, and two kernels are enqueued on stream in
+ * order (dq, which also writes delta, then dk/dv, which reads it); the
+ * result does not depend on
  * scheduling (no atomics). The outputs dq, dk, dv, delta must not overlap
  * each other or any input (FA_ERR_ARG). FA_ERR_HEADDIM for d other than 64,
  * 128 or 256, FA_ERR_DTYPE for fp32 or an unknown dtype; all pointers 16-byte

@@ -11,14 +11,14 @@
 //   dV = P^T dO,  dP = dO V^T,  D_i = sum_c dO_ic O_ic (= sum_j P_ij dP_ij),
 //   dS = P (dP - D),  dQ = scale dS K,  dK = scale dS^T Q.
 //
-// Three kernels on the caller's stream, no atomics (the result does not
+// Two kernels on the caller's stream, no atomics (the result does not
 // depend on scheduling):
-//  * delta_kernel: D = rowsum(dO * O) into the caller's delta buffer;
 //  * dq_kernel: one workgroup per (batch*head, 128-row query tile), built
 //    like the forward: S^T = K Q^T and dP^T = V dO^T on the matrix cores
 //    with Q^T and dO^T held as B operands, P^T and dS^T per lane (each lane
 //    owns one query), then dQ^T += K^T dS^T with K^T read transposed from
-//    LDS and dS^T as the B operand;
+//    LDS and dS^T as the B operand; it first computes its rows'
+//    D = rowsum(dO * O) and writes them to the caller's delta buffer;
 //  * dkdv_kernel: one workgroup per (batch*head, 128-key block), each wave
 //    owning 32 keys with K^T and V^T held as B operands (at d = 256 V^T is
 //    read from an LDS copy of the block's V rows instead); per 32-query
@@ -199,33 +199,6 @@ __device__ __forceinline__ int perm_row(int r, int hh) {
   return 8 * hh + 16 * (r >> 3) + 4 * ((r >> 2) & 1) + (r & 3);
 }
 
-// D_i = sum_c dO_ic O_ic, one row per D/8 consecutive lanes; rows are
-// numbered (b * H + h) * N + i, the layout of Dl.
-template <class T, int D>
-__global__ __launch_bounds__(kThreads) void delta_kernel(const uint16_t* __restrict__ O,
-                                                         const uint16_t* __restrict__ dO,
-                                                         float* __restrict__ Dl, View vo, View vdo, int H,
-                                                         int N, long long rows) {
-  constexpr int TPR = D / 8;
-  constexpr int RPB = kThreads / TPR;
-  const long long row = (long long)blockIdx.x * RPB + threadIdx.x / TPR;
-  const int c = threadIdx.x % TPR;
-  float acc = 0.f;
-  if (row < rows) {
-    const int bh = (int)(row / N), i = (int)(row - (long long)bh * N);
-    const u32x4 a = *(const u32x4*)(O + view_base(vo, bh, H) + (long long)i * vo.r + 8 * c);
-    const u32x4 b = *(const u32x4*)(dO + view_base(vdo, bh, H) + (long long)i * vdo.r + 8 * c);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      acc += to_f32<T>(a[e] & 0xffffu) * to_f32<T>(b[e] & 0xffffu);
-      acc += to_f32<T>(a[e] >> 16) * to_f32<T>(b[e] >> 16);
-    }
-  }
-#pragma unroll
-  for (int o = TPR / 2; o > 0; o >>= 1) acc += __shfl_xor(acc, o, 64);
-  if (c == 0 && row < rows) Dl[row] = acc;
-}
-
 // dQ for one 128-row query tile. Query i sees keys i - wl .. i + wr (wr = 0
 // when causal; an unbounded side is 2^30).
 // Two waves per SIMD (two workgroups per compute unit), within 256 registers.
@@ -234,9 +207,9 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
                           amdgpu_waves_per_eu(D >= 256 ? 1 : 2, D >= 256 ? 1 : 2)))
 void dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
-               const float* __restrict__ LSE, const float* __restrict__ Dl, uint16_t* __restrict__ dQ,
-               View vq, View vk, View vv, View vdo, View vdq, int H, int N, int nqt, int nblocks, float c,
-               float scale, int wl, int wr) {
+               const uint16_t* __restrict__ O, const float* __restrict__ LSE, float* __restrict__ Dl,
+               uint16_t* __restrict__ dQ, View vq, View vk, View vv, View vdo, View vo, View vdq, int H, int N,
+               int nqt, int nblocks, float c, float scale, int wl, int wr) {
   // Two LDS stages, each a K tile then a V tile, filled by direct copies
   // one tile ahead.
   constexpr int TB = kBc * Tile<D>::kRS;
@@ -272,7 +245,25 @@ void dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   }
   // Rows past N get P = 0 (exp2(-inf)) and so contribute nothing.
   const float lse2 = qrow < N ? LSE[qrow] * kLog2e : INFINITY;
-  const float dl = qrow < N ? Dl[qrow] : 0.f;
+  // D_i = sum_c dO_ic O_ic of the lane's row: the lane holds half of the
+  // row's dO (columns 16s + 8hh .. +7), multiplies it with the same columns
+  // of O, and the lane pair (l, l ^ 32) adds the halves. Written to Dl for
+  // the dK/dV kernel, which runs after this one on the same stream.
+  float dl = 0.f;
+  if (qrow < N) {
+    const uint16_t* orow = O + view_base(vo, bh, H) + (long long)qrow * vo.r;
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) {
+      const u32x4 a = *(const u32x4*)(orow + 16 * s + 8 * hh);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        dl += to_f32<T>(a[e] & 0xffffu) * to_f32<T>(gf[s][e] & 0xffffu);
+        dl += to_f32<T>(a[e] >> 16) * to_f32<T>(gf[s][e] >> 16);
+      }
+    }
+  }
+  dl = pair_sum(dl);
+  if (hh == 0 && qrow < N) Dl[qrow] = dl;
 
   const int q_lo = qt * kBr;
   const int t_lo = max(q_lo - wl, 0) / kBc;
@@ -679,20 +670,16 @@ namespace {
 
 template <class T>
 struct BwdKernels {
-  const void* delta;
   const void* dq;
   const void* dkdv;
-  int rows_per_delta_block;
 };
 
 template <class T, int D>
 BwdKernels<T> pick_d(bool causal) {
   // d = 256: V^T read from LDS; otherwise K^T and V^T both in registers.
   constexpr bool VL = D >= 256;
-  return {(const void*)fa::bwd::delta_kernel<T, D>,
-          causal ? (const void*)fa::bwd::dq_kernel<T, D, true> : (const void*)fa::bwd::dq_kernel<T, D, false>,
-          causal ? (const void*)fa::bwd::dkdv_kernel<T, D, true, VL> : (const void*)fa::bwd::dkdv_kernel<T, D, false, VL>,
-          fa::kThreads / (D / 8)};
+  return {causal ? (const void*)fa::bwd::dq_kernel<T, D, true> : (const void*)fa::bwd::dq_kernel<T, D, false>,
+          causal ? (const void*)fa::bwd::dkdv_kernel<T, D, true, VL> : (const void*)fa::bwd::dkdv_kernel<T, D, false, VL>};
 }
 
 template <class T>
@@ -724,7 +711,6 @@ int plan_bwd(const void* q, const void* k, const void* v, const void* o, const f
   const long long tiles = (N + fa::kBr - 1) / fa::kBr;
   const long long blocks = (long long)B * (long long)H * tiles;
   if (blocks > INT_MAX) return FA_ERR_SHAPE;
-  if ((long long)B * H * N > (long long)INT_MAX * (fa::kThreads / 32)) return FA_ERR_SHAPE;  // delta grid
   plan->tiles = tiles;
   plan->blocks = blocks;
   if (blocks == 0) return FA_OK;
@@ -778,28 +764,17 @@ extern "C" int fa_bwd_strided(const void* q, const void* k, const void* v, const
   const long long tiles = plan.tiles, blocks = plan.blocks;
   fa::View* const view = plan.view;
 
-  const void* kd;
   const void* kq;
   const void* kkv;
-  int rpb;
   if (dtype == FA_BF16) {
     const auto kk = pick<fa::Bf16>(d, causal != 0);
-    kd = kk.delta, kq = kk.dq, kkv = kk.dkdv, rpb = kk.rows_per_delta_block;
+    kq = kk.dq, kkv = kk.dkdv;
   } else {
     const auto kk = pick<fa::F16>(d, causal != 0);
-    kd = kk.delta, kq = kk.dq, kkv = kk.dkdv, rpb = kk.rows_per_delta_block;
+    kq = kk.dq, kkv = kk.dkdv;
   }
   hipStream_t st = (hipStream_t)stream;
-
-  const long long rows = (long long)B * H * N;
   int h_arg = H, n_arg = N;
-  long long nrows = rows;
-  void* dargs[] = {(void*)&o, (void*)&dout, (void*)&delta, (void*)&view[3], (void*)&view[4],
-                   (void*)&h_arg, (void*)&n_arg, (void*)&nrows};
-  const long long dblocks = (rows + rpb - 1) / rpb;
-  if (dblocks > INT_MAX) return FA_ERR_SHAPE;
-  if (hipLaunchKernel(kd, dim3((unsigned)dblocks), dim3(fa::kThreads), dargs, 0, st) != hipSuccess)
-    return FA_ERR_LAUNCH;
 
   constexpr int kUnbounded = 1 << 30;
   int wl = window_left < 0 ? kUnbounded : window_left;
@@ -808,13 +783,15 @@ extern "C" int fa_bwd_strided(const void* q, const void* k, const void* v, const
   float c = (float)((double)scale * 1.4426950408889634074);
   float sc = scale;
   int nt = (int)tiles, nb = (int)blocks;
-  const float* delta_c = delta;
-  void* qargs[] = {(void*)&q,       (void*)&k,       (void*)&v,       (void*)&dout,    (void*)&lse,
-                   (void*)&delta_c, (void*)&dq,      (void*)&view[0], (void*)&view[1], (void*)&view[2],
-                   (void*)&view[4], (void*)&view[5], (void*)&h_arg,   (void*)&n_arg,   (void*)&nt,
-                   (void*)&nb,      (void*)&c,       (void*)&sc,      (void*)&wl,      (void*)&wr};
+  // dq_kernel writes the row sums D into delta; dkdv_kernel reads them.
+  void* qargs[] = {(void*)&q,       (void*)&k,       (void*)&v,       (void*)&dout,    (void*)&o,
+                   (void*)&lse,     (void*)&delta,   (void*)&dq,      (void*)&view[0], (void*)&view[1],
+                   (void*)&view[2], (void*)&view[4], (void*)&view[3], (void*)&view[5], (void*)&h_arg,
+                   (void*)&n_arg,   (void*)&nt,      (void*)&nb,      (void*)&c,       (void*)&sc,
+                   (void*)&wl,      (void*)&wr};
   if (hipLaunchKernel(kq, dim3((unsigned)blocks), dim3(fa::kThreads), qargs, 0, st) != hipSuccess)
     return FA_ERR_LAUNCH;
+  const float* delta_c = delta;
   void* kargs[] = {(void*)&q,       (void*)&k,       (void*)&v,       (void*)&dout,    (void*)&lse,
                    (void*)&delta_c, (void*)&dk,      (void*)&dv,      (void*)&view[0], (void*)&view[1],
                    (void*)&view[2], (void*)&view[4], (void*)&view[6], (void*)&view[7], (void*)&h_arg,
