@@ -622,7 +622,7 @@ def main():
                          "flops_counted": "4*d per visible (query, key) pair", "parity_ok": parw["ok"],
                          "max_abs_dO": parw["err_o"], "max_abs_dLSE": parw["err_l"]}
     if not args.no_secondary:
-        # Backward pass on the GPT-3-shaped workload (fa_bwd: delta, dQ and
+        # Backward pass on the GPT-3-shaped workload (fa_bwd: dQ with the row sums D, and
         # dK/dV kernels), parity-checked on 2 of the 128 heads first.
         # Flops: 2.5x the forward's (the five N x N x d products of the
         # gradient, halved for causal), the usual accounting.
