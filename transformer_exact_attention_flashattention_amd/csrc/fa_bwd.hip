@@ -370,7 +370,7 @@ void dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
 }
 
 // Query rows per step of the dK/dV kernel: 64, or 32 at d = 256 so that
-// three stages fit in LDS.
+// the stages (of 512-byte rows) fit in LDS beside the copy of V.
 template <int D>
 constexpr int dkdv_step_rows() {
   return D >= 256 ? 32 : 64;
@@ -380,8 +380,8 @@ constexpr int kStatSlots = 64;  // LDS floats reserved for LSE (and for delta) p
 // dK and dV for one 128-key block; wave w owns keys 32w .. 32w+31 of it.
 // One wave per SIMD: K^T, V^T and the dK^T, dV^T accumulators alone take
 // 192 registers per lane at d = 128. Query tiles (Q, dO, LSE, delta) stream
-// through a ring of three LDS stages filled by direct copies issued two
-// steps ahead.
+// through a ring of LDS stages filled by direct copies: three stages,
+// issued two steps ahead, at d <= 128.
 // VL (d = 256): V^T is read from an LDS copy of the block's V rows instead
 // of registers. At d = 256 the two accumulators and the K^T, V^T operands
 // do not fit the registers together (held all in registers, the kernel
