@@ -1,9 +1,19 @@
 """Randomised GPU parity: 48 forward cases drawn with a fixed seed over every
 option at once (dtype, head dim, batch, heads, query and key lengths,
 causal, window, split-KV parts, strided operands), each against the fp64
-oracle with the bounds of test_gpu_parity.py, and 16 backward cases against
-the gradient oracle with the bounds of test_gpu_bwd.py. The draw is printed
-with each case, so a failure names its configuration."""
+oracle, and 16 backward cases against the gradient oracle with the bounds of
+test_gpu_bwd.py. The draw is printed with each case, so a failure names its
+configuration.
+
+Forward bound: the stated tolerance (2e-3 fp16, 1e-2 bf16, 1e-5 fp32) times
+max(1, max|O_oracle|). The draws include rows that see only a few keys
+(narrow windows, a window's first rows), whose output is close to single V
+rows, |O| up to 3-4 with unit-variance V. Both roundings of the 16-bit path,
+of P to the input type and of O to the output type, scale with those
+magnitudes (up to u (|O| + max|V|), u = 2^-8 for bf16, 2^-11 for fp16), so
+the absolute bound, which holds where O averages many keys, is taken
+relative to |O| when |O| exceeds 1 (a bf16 row that sees 3 keys measured
+1.13e-2 at |O| near 3)."""
 
 import math
 import sys
@@ -71,7 +81,8 @@ def test_forward_fuzz(i):
                                  window=c["window"])
     o64, l64 = o.double().cpu().numpy(), lse.double().cpu().numpy()
     assert np.isfinite(o64).all() and np.isfinite(l64).all()
-    assert np.abs(o64 - o_ref).max() <= TOL_O[c["dtype"]]
+    err_o = np.abs(o64 - o_ref).max()
+    assert err_o <= TOL_O[c["dtype"]] * max(1.0, np.abs(o_ref).max()), err_o
     assert np.abs(l64 - l_ref).max() <= TOL_LSE
 
 
