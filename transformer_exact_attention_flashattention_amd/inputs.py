@@ -70,6 +70,15 @@ def make_config(cfg, seed=42):
     return make_qkv(c["B"], c["H"], c["N"], c["D"], c["dtype"], seed)
 
 
+def make_cycled_heads(B, H, N, D, dtype, period, seed=42, device="cpu"):
+    """Q, K, V [B, H, N, D] whose B*H heads repeat a pool of ``period``
+    distinct seeded heads: flat head b*H + h is head (b*H + h) % period of
+    ``make_qkv(1, period, N, D, dtype, seed)``. Builds tensors of many GB
+    cheaply; the gather runs on ``device``."""
+    idx = torch.arange(B * H, device=device) % period
+    return tuple(p[0].to(device)[idx].view(B, H, N, D) for p in make_qkv(1, period, N, D, dtype, seed))
+
+
 def digest(*tensors):
     """SHA-256 over the raw bytes of the given CPU tensors (input provenance)."""
     h = hashlib.sha256()
