@@ -423,11 +423,12 @@ def bench_decode(fa, inputs, dev, stream, steps, warmup, no_parity):
             "max_abs_dLSE": err_l}
 
 
-def bench_sweep(fa, inputs, dev, stream, no_parity):
+def bench_sweep(fa, inputs, dev, stream, no_parity, dtype="bf16"):
     """Forward TFLOP/s over sequence lengths 2k-16k, head dimensions 64, 128
-    and 256, with and without the causal mask (bf16; one batch of
-    2^18 / N heads, so every call has 2^18 query rows). Each shape is first
-    checked against the oracle on 4 rows of its first head."""
+    and 256, with and without the causal mask (bf16 or f16 inputs; one batch
+    of 2^18 / N heads, so every call has 2^18 query rows). Each shape is
+    first checked against the oracle on 4 rows of its first head, to the
+    parity bound of its dtype."""
     import numpy as np
     import torch
 
@@ -435,7 +436,7 @@ def bench_sweep(fa, inputs, dev, stream, no_parity):
     for D in (64, 128, 256):
         for N in (2048, 4096, 8192, 16384):
             H = (1 << 18) // N
-            q, k, v = inputs.make_qkv(1, H, N, D, "bf16", seed=N + D)
+            q, k, v = inputs.make_qkv(1, H, N, D, dtype, seed=N + D)
             qd, kd, vd = (t.to(dev) for t in (q, k, v))
             o = torch.empty_like(qd)
             lse = torch.empty(qd.shape[:3], dtype=torch.float32, device=dev)
@@ -451,14 +452,14 @@ def bench_sweep(fa, inputs, dev, stream, no_parity):
                     rows = np.array([0, 1, N // 2, N - 1])
                     err_o, err_l = check_parity(o[:, :1].cpu(), lse[:, :1].cpu(), q[:, :1], k[:, :1], v[:, :1], scale,
                                                 causal, rows)
-                    ok = err_o <= 1e-2 and err_l <= 1e-3
+                    ok = err_o <= (1e-2 if dtype == "bf16" else 2e-3) and err_l <= 1e-3
                 _, per = time_launches(step, stream, 10, 5, settle_ms=600.0)
                 ms = float(np.mean(per))
                 fl = 4.0 * H * N * N * D / (2 if causal else 1)
-                res.append({"N": N, "H": H, "d": D, "causal": causal, "kernel_ms_mean": round(ms, 4),
+                res.append({"N": N, "H": H, "d": D, "causal": causal, "dtype": dtype, "kernel_ms_mean": round(ms, 4),
                             "tflops": round(fl / (ms * 1e-3) / 1e12, 1),
                             "frac": round(fl / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4), "parity_ok": ok})
-                log(f"[sweep] N={N} H={H} d={D} causal={causal}: {ms:.4f} ms, {res[-1]['tflops']} TFLOP/s")
+                log(f"[sweep] {dtype} N={N} H={H} d={D} causal={causal}: {ms:.4f} ms, {res[-1]['tflops']} TFLOP/s")
             del qd, kd, vd, o, lse
     return res
 
@@ -477,7 +478,9 @@ def main():
                          "(outside the events): a cold-cache figure")
     ap.add_argument("--sweep", action="store_true",
                     help="instead of the standard line, print one JSON line with the forward's TFLOP/s over "
-                         "N = 2k..16k, d = 64/128/256, causal or not (bf16)")
+                         "N = 2k..16k, d = 64/128/256, causal or not (--sweep-dtype, bf16 by default)")
+    ap.add_argument("--sweep-dtype", choices=("bf16", "f16"), default="bf16",
+                    help="input type of the --sweep shapes (the fp16 and bf16 matrix peaks are the same)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 1 GiB device-to-device copy 3 times, to scale HBM counters")
     args = ap.parse_args()
@@ -500,9 +503,9 @@ def main():
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream(dev)
     if args.sweep:
-        sweep = bench_sweep(fa, inputs, dev, stream, args.no_parity)
-        print(json.dumps({"sweep": sweep, "unit": "TFLOP/s", "peak": PEAK_BF16_TFLOPS, "dtype": "bf16",
-                          "data": "synthetic: i.i.d. N(0,1) Q, K, V cast to bf16"}), flush=True)
+        sweep = bench_sweep(fa, inputs, dev, stream, args.no_parity, args.sweep_dtype)
+        print(json.dumps({"sweep": sweep, "unit": "TFLOP/s", "peak": PEAK_BF16_TFLOPS, "dtype": args.sweep_dtype,
+                          "data": f"synthetic: i.i.d. N(0,1) Q, K, V cast to {args.sweep_dtype}"}), flush=True)
         sys.exit(1 if any(r["parity_ok"] is False for r in sweep) else 0)
 
     def run_config(cfg, steps, warmup, check_rows, window=(-1, -1), settle_ms=600.0):
