@@ -32,6 +32,13 @@ def test_more_than_one_gpu_is_refused():
     assert r.stdout == ""  # no JSON line for a run that did not happen
 
 
+def test_sweep_dtype_is_checked_before_any_gpu_work():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--sweep", "--sweep-dtype", "f32"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2 and "--sweep-dtype" in r.stderr
+    assert r.stdout == ""
+
+
 def test_metric_flops(bench):
     c = {"B": 1, "H": 16, "N": 16384, "D": 256, "causal": True}
     assert bench.metric_flops(c) == 4.0 * 16 * 16384 ** 2 * 256 / 2
