@@ -1,8 +1,10 @@
 """Randomised GPU parity: 48 forward cases drawn with a fixed seed over every
 option at once (dtype, head dim, batch, heads, query and key lengths,
-causal, window, split-KV parts, strided operands), each against the fp64
-oracle, and 16 backward cases against the gradient oracle with the bounds of
-test_gpu_bwd.py. The draw is printed with each case, so a failure names its
+causal, window, split-KV parts, strided operands, scale), each against the
+fp64 oracle, and 16 backward cases (dtype, head dim, batch, heads, length,
+causal, window, strided operands, scale) against the gradient oracle with
+the bounds of test_gpu_bwd.py. The scale is 1/sqrt(d) times one of 1, 0.5,
+2.5 or -1. The draw is printed with each case, so a failure names its
 configuration.
 
 Forward bound: the stated tolerance (2e-3 fp16, 1e-2 bf16, 1e-5 fp32) times
@@ -13,7 +15,9 @@ of P to the input type and of O to the output type, scale with those
 magnitudes (up to u (|O| + max|V|), u = 2^-8 for bf16, 2^-11 for fp16), so
 the absolute bound, which holds where O averages many keys, is taken
 relative to |O| when |O| exceeds 1 (a bf16 row that sees 3 keys measured
-1.13e-2 at |O| near 3)."""
+1.13e-2 at |O| near 3). In fp32 the rounding of the scores and of the
+exponent arguments grows with the logit spread, so the fp32 bound is also
+widened by max(1, |scale| sqrt(d)), as in test_gpu_parity.py."""
 
 import math
 import sys
@@ -57,8 +61,9 @@ def draw_forward(i):
         window = (int(rng.choice([-1, 0, 5, 80, 300])), int(rng.choice([-1, 0, 7, 120])))
     splits = int(rng.choice([1, 1, 0, 2, 5]))
     layout = str(rng.choice(["bhnd", "bnhd"]))
+    smul = float(rng.choice([1.0, 1.0, 0.5, 2.5, -1.0]))  # scale = smul / sqrt(d)
     return dict(dtype=dtype, D=D, B=B, H=H, N=N, Nk=Nk, causal=causal, window=window, splits=splits,
-                layout=layout)
+                layout=layout, smul=smul)
 
 
 @pytest.mark.parametrize("i", range(48))
@@ -74,15 +79,18 @@ def test_forward_fuzz(i):
         qd, kd, vd = (t.cuda() for t in (q, k, v))
     o = torch.full(q.shape, float("nan"), dtype=q.dtype, device="cuda")
     lse = torch.full(q.shape[:3], float("nan"), device="cuda")
-    fa.fwd(qd, kd, vd, causal=c["causal"], window_size=c["window"], out=o, lse=lse, num_splits=c["splits"])
+    scale = c["smul"] / math.sqrt(c["D"])
+    fa.fwd(qd, kd, vd, softmax_scale=scale, causal=c["causal"], window_size=c["window"], out=o, lse=lse,
+           num_splits=c["splits"])
     torch.cuda.synchronize()
-    scale = 1.0 / math.sqrt(c["D"])
     o_ref, l_ref = attention_ref(q.double().numpy(), k.double().numpy(), v.double().numpy(), scale, c["causal"],
                                  window=c["window"])
     o64, l64 = o.double().cpu().numpy(), lse.double().cpu().numpy()
     assert np.isfinite(o64).all() and np.isfinite(l64).all()
     err_o = np.abs(o64 - o_ref).max()
-    assert err_o <= TOL_O[c["dtype"]] * max(1.0, np.abs(o_ref).max()), err_o
+    # fp32: the rounding of scores and exponent arguments grows with the logit spread |smul|
+    widen = max(1.0, abs(c["smul"])) if c["dtype"] == "f32" else 1.0
+    assert err_o <= TOL_O[c["dtype"]] * widen * max(1.0, np.abs(o_ref).max()), err_o
     assert np.abs(l64 - l_ref).max() <= TOL_LSE
 
 
@@ -91,7 +99,8 @@ def draw_backward(i):
     return dict(dtype=str(rng.choice(["f16", "bf16"])), D=int(rng.choice([64, 128, 256])),
                 B=int(rng.integers(1, 3)), H=int(rng.integers(1, 3)), N=int(rng.choice([1, 33, 128, 200, 513])),
                 causal=bool(rng.random() < 0.5),
-                window=(-1, -1) if rng.random() < 0.6 else (int(rng.choice([0, 9, 100])), int(rng.choice([-1, 4]))))
+                window=(-1, -1) if rng.random() < 0.6 else (int(rng.choice([0, 9, 100])), int(rng.choice([-1, 4]))),
+                layout=str(rng.choice(["bhnd", "bnhd"])), smul=float(rng.choice([1.0, 1.0, 0.5, 2.5, -1.0])))
 
 
 @pytest.mark.parametrize("i", range(16))
@@ -101,12 +110,16 @@ def test_backward_fuzz(i):
     sys.__stderr__.flush()
     q, k, v = inputs.make_qkv(c["B"], c["H"], c["N"], c["D"], c["dtype"], seed=i + 3000)
     do = torch.randn(q.shape, generator=torch.Generator().manual_seed(i)).to(q.dtype)
-    qd, kd, vd, dod = (t.cuda() for t in (q, k, v, do))
-    o, lse = fa.fwd(qd, kd, vd, causal=c["causal"], window_size=c["window"])
-    grads = fa.bwd(qd, kd, vd, o, lse, dod, causal=c["causal"], window_size=c["window"])
+    if c["layout"] == "bnhd":  # [B, N, H, d] storage, passed as transposed views
+        qd, kd, vd, dod = (t.transpose(1, 2).contiguous().cuda().transpose(1, 2) for t in (q, k, v, do))
+    else:
+        qd, kd, vd, dod = (t.cuda() for t in (q, k, v, do))
+    scale = c["smul"] / math.sqrt(c["D"])
+    o, lse = fa.fwd(qd, kd, vd, softmax_scale=scale, causal=c["causal"], window_size=c["window"])
+    grads = fa.bwd(qd, kd, vd, o, lse, dod, softmax_scale=scale, causal=c["causal"], window_size=c["window"])
     torch.cuda.synchronize()
     ref = attention_bwd_ref(q.double().numpy(), k.double().numpy(), v.double().numpy(), do.double().numpy(),
-                            1.0 / math.sqrt(c["D"]), c["causal"], c["window"])
+                            scale, c["causal"], c["window"])
     for got, r in zip(grads, ref):
         g = got.double().cpu().numpy()
         assert np.isfinite(g).all()
