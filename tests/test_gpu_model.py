@@ -1,0 +1,138 @@
+"""The 16-bit forward kernel (through the C ABI) against the CPU model of its
+roundings (tests/kernel_model.py), element by element.
+
+The fp64 oracle is the parity bar (test_gpu_parity.py). This test sits
+beside it: on bf16 workloads the output's own rounding (half a unit in the
+last place of |O| near 2 is 7.8e-3) uses most of the 1e-2 bar, so a kernel
+error of a few 1e-4 would pass the oracle test unseen. The model rounds at
+the same places as the kernel (P to the input type before the PV product,
+O once at the end, the same lazy exponent reference, fp32 everywhere else),
+so the kernel may differ from it only by the order of fp32 additions inside
+the matrix products and row sums, and by the hardware exp2:
+
+* each such difference is a few fp32 units in the last place of a value
+  before it is rounded to 16 bits, so the 16-bit rounding of O flips for a
+  few elements (one unit of the output type), and
+* the rounding of P flips for a few of the N^2 scores; one flip moves O_ic
+  by one spacing of P times |V_jc| / l, i.e. u' P_ij |V_jc| with u' = 2^-7
+  (bf16) or 2^-10 (fp16), which is below one unit of O except in rows whose
+  softmax sits on a few keys.
+
+Bound per element: |O - O_model| <= 2 ulp(O_model) + 2 u' (max_j P_ij)
+(max_j |V_jc|) (P from the oracle), and the share of elements that differ at all must
+be small (< 2%). A kernel error of 1e-4 in a row that averages many keys
+(|O| ~ 0.05, ulp 2.4e-4 in bf16) breaks the bound by itself.
+"""
+
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import transformer_exact_attention_flashattention_amd as fa
+from transformer_exact_attention_flashattention_amd import build as fabuild
+from transformer_exact_attention_flashattention_amd import inputs
+from oracle import scores_ref, softmax_rows_ref
+
+from kernel_model import forward_model, output_ulp
+
+pytestmark = pytest.mark.gpu
+
+SPACING_P = {torch.bfloat16: 2.0 ** -7, torch.float16: 2.0 ** -10}  # spacing of [1, 2) in the input type
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu_ready():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+    if not fabuild.is_built():
+        fabuild.build()
+    fa.lib()
+
+
+def max_p(q, k, scale, causal, window, heads):
+    """max_j P_ij per row for the first `heads` heads (fp64, from the oracle)."""
+    B, _, N, _ = q.shape
+    out = np.empty((B, heads, N))
+    for b in range(B):
+        for h in range(heads):
+            for r0 in range(0, N, 1024):
+                rows = np.arange(r0, min(r0 + 1024, N))
+                s = scores_ref(q[b, h].double().numpy(), k[b, h].double().numpy(), scale, causal, rows, window)
+                p, _, _ = softmax_rows_ref(s)
+                out[b, h, r0:r0 + len(rows)] = p.max(axis=1)
+    return out
+
+
+def compare(q, k, v, scale, causal=False, window=(-1, -1), heads=None, label=""):
+    qd, kd, vd = (t.cuda() for t in (q, k, v))
+    o = torch.full_like(qd, float("nan"))
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device="cuda")
+    fa.fwd(qd, kd, vd, softmax_scale=scale, causal=causal, window_size=window, out=o, lse=lse, num_splits=1)
+    torch.cuda.synchronize()
+    heads = q.shape[1] if heads is None else heads
+    q, k, v = q[:, :heads], k[:, :heads], v[:, :heads]
+    og = o[:, :heads].cpu().double().numpy()
+    om, lm = forward_model(q, k, v, scale, causal, window)
+    om = om.double().numpy()
+    d = np.abs(og - om)
+    ulp = output_ulp(om, q.dtype)
+    vmax = np.abs(v.double().numpy()).max(axis=2, keepdims=True)  # max_j |V_jc| per column
+    bound = 2 * ulp + 2 * SPACING_P[q.dtype] * max_p(q, k, scale, causal, window, heads)[..., None] * vmax
+    frac = float((d > 0).mean())
+    dl = float(np.abs(lse[:, :heads].cpu().double().numpy() - lm.double().numpy()).max())
+    sys.__stderr__.write(f"[model] {label}: max|dO|={d.max():.3e} max ulps={(d / ulp).max():.2f} "
+                         f"worst/bound={(d / bound).max():.3f} differing={frac:.2e} max|dLSE|={dl:.2e}\n")
+    sys.__stderr__.flush()
+    assert np.isfinite(og).all()
+    assert (d <= bound).all(), f"{label}: worst ratio to the bound {(d / bound).max():.3f}"
+    assert frac < 0.02, f"{label}: {frac:.3%} of the elements differ from the model"
+    assert dl <= 1e-5, f"{label}: LSE differs from the model by {dl:.2e}"
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 4])
+def test_configs_against_model(cfg):
+    c = inputs.CONFIGS[cfg]
+    q, k, v = inputs.make_config(cfg)
+    compare(q, k, v, 1.0 / math.sqrt(c["D"]), c["causal"], label=f"config {cfg}")
+
+
+def test_long_causal_d256_against_model():
+    """The full 16-head launch; the first 2 heads against the model."""
+    c = inputs.CONFIGS[5]
+    q, k, v = inputs.make_config(5)
+    compare(q, k, v, 1.0 / math.sqrt(c["D"]), True, heads=2, label="config 5, heads 0-1")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("D", [64, 128, 256])
+def test_shapes_against_model(dtype, D):
+    for N, causal, window in ((1, False, (-1, -1)), (17, True, (-1, -1)), (130, False, (-1, -1)),
+                              (257, True, (-1, -1)), (1000, True, (-1, -1)), (700, False, (80, 7)),
+                              (700, True, (300, -1))):
+        q, k, v = inputs.make_qkv(1, 2, N, D, dtype, seed=N + D)
+        compare(q, k, v, 1.0 / math.sqrt(D), causal, window, label=f"{dtype} d={D} N={N} causal={causal} "
+                                                                    f"window={window}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_scales_and_moves_against_model(dtype):
+    """Other scales (zero, negative, peaky) and keys whose norms grow along
+    the sequence, which make many rows move their exponent reference."""
+    D, N = 128, 700
+    q, k, v = inputs.make_qkv(1, 2, N, D, dtype, seed=31)
+    for smul in (0.0, -1.0, 2.5):
+        compare(q, k, v, smul / math.sqrt(D), True, label=f"{dtype} scale {smul}/sqrt(d)")
+    ramp = torch.linspace(0.05, 4.0, N).view(1, 1, N, 1)
+    k2 = (k.float() * ramp).to(k.dtype)
+    compare(q, k2, v, 2.0 / math.sqrt(D), False, label=f"{dtype} growing logits")
+    compare(q, k2, v, 2.0 / math.sqrt(D), True, (300, -1), label=f"{dtype} growing logits, window")
+
+
+def test_fewer_queries_than_keys_against_model():
+    q = inputs.make_qkv(1, 3, 130, 128, "bf16", seed=5)[0]
+    _, k, v = inputs.make_qkv(1, 3, 777, 128, "bf16", seed=6)
+    compare(q, k, v, 1.0 / math.sqrt(128), True, label="N=130 against Nk=777, causal")
+    compare(q, k, v, 1.0 / math.sqrt(128), False, (100, 20), label="N=130 against Nk=777, window")

@@ -311,9 +311,11 @@ __device__ __forceinline__ float pair_sum(float x) {
 // The exponent reference m (log2 units) need not be the exact running max:
 // the result is the same in exact arithmetic for any reference (the final
 // division by the running sum cancels it), and fp32/bf16 only need the P
-// values bounded. m therefore stays put while every P of a tile is at most
-// 2^kTau, which spares both the row max and the rescale of the output
-// accumulator on most tiles; it moves to the true running max otherwise.
+// values bounded. A row's m therefore stays put while the row's P sum over
+// a 64-key tile is at most 2^kTau (so every P is), which spares both the
+// row max and the rescale of the output accumulator on most tiles; it moves
+// to the row's true running max otherwise. The first reference is the
+// row's max over the first key tile of its query block.
 constexpr float kTau = 8.0f;
 constexpr float kTauPow = 256.0f;  // 2^kTau
 
@@ -654,12 +656,17 @@ void fwd16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K
     }
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_setprio(0);
-    // Some P of the tile may exceed 2^kTau (or m_run was still -inf): move
-    // the reference to the running max and redo P (rare). A row that has
-    // seen no visible key yet (possible with a window) keeps m = -inf and
-    // gets P = 0 and l = 0 from a finite stand-in reference.
-    if (__builtin_amdgcn_ballot_w64(!(ls <= kTauPow)) != 0) {
-      const float m_new = fmaxf(m_run, tile_max());
+    // A row whose P sum over the tile's 64 keys exceeds 2^kTau (or whose m
+    // was still -inf: then the sum is NaN or inf) moves its reference to
+    // its running max and redoes P (rare). The move is per row: the other
+    // rows of the wave keep m, recompute the same P and scale by
+    // exp2(0) = 1, so a row's result depends on its own keys only. A row
+    // that has seen no visible key yet (possible with a window) keeps
+    // m = -inf and gets P = 0 and l = 0 from a finite stand-in reference.
+    const bool need = !(pair_sum(ls) <= kTauPow);
+    if (__builtin_amdgcn_ballot_w64(need) != 0) {
+      const float tmax = tile_max();
+      const float m_new = need ? fmaxf(m_run, tmax) : m_run;
       const float m_use = m_new == -INFINITY ? 0.f : m_new;
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
       m_run = m_new;
