@@ -18,10 +18,14 @@ the matrix products and row sums, and by the hardware exp2:
   (bf16) or 2^-10 (fp16), which is below one unit of O except in rows whose
   softmax sits on a few keys.
 
-Bound per element: |O - O_model| <= 2 ulp(O_model) + 2 u' (max_j P_ij)
-(max_j |V_jc|) (P from the oracle), and the share of elements that differ at all must
-be small (< 2%). A kernel error of 1e-4 in a row that averages many keys
-(|O| ~ 0.05, ulp 2.4e-4 in bf16) breaks the bound by itself.
+Bounds: per element |O - O_model| <= 2 ulp(O_model) + 2 u' (max_j P_ij)
+(max_j |V_jc|) (P from the oracle), which a sporadic error of a few units
+breaks; and the share of elements that differ at all must stay below 2%
+in bf16 (measured at most 0.7%) and 5% in fp16 (at most 1.7%), which a
+small systematic error breaks: an error of 1e-4 before the output rounding,
+in rows that average many keys (|O| about 0.05, where one bf16 unit is
+2.4e-4 and one fp16 unit 3e-5), would change the rounded output of about
+40% (bf16) or nearly all (fp16) of those elements.
 """
 
 import math
@@ -41,6 +45,9 @@ from kernel_model import forward_model, output_ulp
 pytestmark = pytest.mark.gpu
 
 SPACING_P = {torch.bfloat16: 2.0 ** -7, torch.float16: 2.0 ** -10}  # spacing of [1, 2) in the input type
+# Largest share of output elements allowed to differ from the model (measured
+# at most 0.7% in bf16 and 1.7% in fp16, whose finer spacing flips more often).
+MAX_DIFFERING = {torch.bfloat16: 0.02, torch.float16: 0.05}
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -88,8 +95,10 @@ def compare(q, k, v, scale, causal=False, window=(-1, -1), heads=None, label="")
     sys.__stderr__.flush()
     assert np.isfinite(og).all()
     assert (d <= bound).all(), f"{label}: worst ratio to the bound {(d / bound).max():.3f}"
-    assert frac < 0.02, f"{label}: {frac:.3%} of the elements differ from the model"
-    assert dl <= 1e-5, f"{label}: LSE differs from the model by {dl:.2e}"
+    assert frac < MAX_DIFFERING[q.dtype], f"{label}: {frac:.3%} of the elements differ from the model"
+    # LSE = (m + log2 l) ln 2 in fp32 on both sides: a few fp32 units of |LSE|
+    lmax = float(np.abs(lm.double().numpy()).max())
+    assert dl <= 1e-6 + 2.0 ** -21 * lmax, f"{label}: LSE differs from the model by {dl:.2e}"
 
 
 @pytest.mark.parametrize("cfg", [1, 2, 4])
