@@ -45,7 +45,8 @@ typedef enum {
     FA_ERR_DTYPE = -4,   /* dtype is not an fa_dtype */
     FA_ERR_ALIGN = -5,   /* a row of q, k, v, o not 16-byte aligned, or lse not 4-byte aligned */
     FA_ERR_ARG = -6,     /* causal not 0/1, scale not finite, or an output overlaps */
-    FA_ERR_LAUNCH = -7   /* the HIP runtime rejected the kernel launch */
+    FA_ERR_LAUNCH = -7,  /* the HIP runtime rejected the kernel launch */
+    FA_ERR_SCRATCH = -8  /* fa_fwd_kv_noalloc: the partial results exceed its static scratch buffer */
 } fa_status;
 
 /*
@@ -200,6 +201,35 @@ int fa_fwd_kv(const void* q, const void* k, const void* v, void* o, float* lse,
               const long long* strides, void* workspace, long long workspace_bytes,
               int num_splits, int B, int H, int N, int Nk, int d, float scale, int causal,
               int window_left, int window_right, int dtype, void* stream);
+
+/*
+ * fa_fwd_kv_noalloc - fa_fwd_kv without a workspace argument, for callers
+ * that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): with more than one part
+ * the partial results go to a static device array of the library,
+ * FA_NOALLOC_SCRATCH_BYTES long, instead of a caller workspace. The call
+ * itself allocates nothing (no hipMalloc, hipFree or allocating library
+ * routine); the caller still passes q, k, v, o and lse.
+ *
+ * The array exists once per GPU the library runs on (each GPU holds its
+ * own copy, looked up on the first call on that device, with that device
+ * current) and is held until the process ends. Every call on one GPU shares
+ * it: calls that overlap in time on one GPU (on different streams, or from
+ * different threads) race on it and must be ordered by the caller. Its
+ * previous contents never matter: every element a call reads is written by
+ * that call first. `stream` must belong to the current device.
+ *
+ * Arguments, result and errors as fa_fwd_kv, and: FA_ERR_SCRATCH (before
+ * any HIP call) when the parts' partial results, 4 * S * B * H * N * (d + 1)
+ * bytes for S parts (fa_fwd_splitkv_workspace), exceed
+ * FA_NOALLOC_SCRATCH_BYTES; FA_ERR_LAUNCH if the device or the array's
+ * address cannot be obtained.
+ */
+#define FA_NOALLOC_SCRATCH_BYTES (64ll << 20)
+int fa_fwd_kv_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                      const long long* strides, int num_splits, int B, int H, int N, int Nk, int d,
+                      float scale, int causal, int window_left, int window_right, int dtype,
+                      void* stream);
 
 /*
  * fa_fwd_num_splits - host-only: the number of parts fa_fwd_splitkv uses

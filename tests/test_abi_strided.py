@@ -323,3 +323,31 @@ def test_fwd_kv_num_splits_for_decode():
     assert fa.splitkv_num_splits(4, 64, 2048, 128, True, Nk=4096) == 1
     # matrix-core bound shapes keep filling the resident slots (at most 16)
     assert fa.splitkv_num_splits(1, 1, 16384, 128, True) == 4
+
+
+# ------------------------------------------- the allocation-free forward --
+
+def fwd_noalloc(N, Nk, splits, causal=0, B=1, H=2, d=64, step=0x100_0000):
+    ptrs = [step, 2 * step, 3 * step, 4 * step, 5 * step]
+    return fa.fa_fwd_kv_noalloc(*ptrs, None, splits, B, H, N, Nk, d, 0.125, causal, -1, -1, fa.FA_BF16)
+
+
+def test_noalloc_rejects_partials_beyond_its_scratch_before_any_hip_call():
+    # 16 parts of 64 heads x 4096 rows x (256 + 1) floats: 4.3 GB > 64 MiB
+    assert fwd_noalloc(4096, 4096, 16, B=1, H=64, d=256, step=0x1000_0000) == -8
+    # one byte-count past the limit is refused, the largest that fits is not checked here (it would launch)
+    need = 4 * 2 * 1 * 64 * 1024 * (256 + 1)  # 2 parts, 64 heads, 1024 rows, d = 256
+    assert need > fa.NOALLOC_SCRATCH_BYTES
+    assert fwd_noalloc(1024, 1024, 2, H=64, d=256, step=0x1000_0000) == -8
+    assert "scratch" in fa.strerror(-8)
+
+
+@pytest.mark.parametrize("N,Nk,splits,causal,code", [
+    (5, 100, -1, 0, ARG), (5, 100, 65, 0, ARG),
+    (5, 0, 2, 0, ARG),            # no key at all
+    (8, 4, 2, 1, ARG),            # causal: rows before the first key
+    (5, -1, 2, 0, SHAPE),
+    (0, 0, 2, 1, OK),             # nothing to do
+])
+def test_noalloc_shares_the_checks(N, Nk, splits, causal, code):
+    assert fwd_noalloc(N, Nk, splits, causal) == code

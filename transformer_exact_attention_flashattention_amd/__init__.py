@@ -60,11 +60,15 @@ STATUS = {
     -5: "FA_ERR_ALIGN",
     -6: "FA_ERR_ARG",
     -7: "FA_ERR_LAUNCH",
+    -8: "FA_ERR_SCRATCH",
 }
 # Every symbol include/fa.h declares.
 EXPORTS = ("fa_fwd", "fa_fwd_window", "fa_fwd_strided", "fa_bwd", "fa_bwd_strided", "fa_strerror",
            "fa_fwd_grid", "fa_fwd_strided_check", "fa_bwd_strided_check", "fa_fwd_splitkv",
-           "fa_fwd_num_splits", "fa_fwd_splitkv_workspace", "fa_fwd_kv", "fa_fwd_kv_num_splits")
+           "fa_fwd_num_splits", "fa_fwd_splitkv_workspace", "fa_fwd_kv", "fa_fwd_kv_num_splits",
+           "fa_fwd_kv_noalloc")
+# Bytes of the static device array behind fa_fwd_kv_noalloc (FA_NOALLOC_SCRATCH_BYTES).
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 _lib = None
 
@@ -121,6 +125,12 @@ def lib() -> ctypes.CDLL:
         h.fa_fwd_kv.restype = ctypes.c_int
         h.fa_fwd_kv.argtypes = [ctypes.c_void_p] * 5 + [
             ctypes.POINTER(ctypes.c_longlong), ctypes.c_void_p, ctypes.c_longlong, ctypes.c_int,
+            ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_float,
+            ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+        ]
+        h.fa_fwd_kv_noalloc.restype = ctypes.c_int
+        h.fa_fwd_kv_noalloc.argtypes = [ctypes.c_void_p] * 5 + [
+            ctypes.POINTER(ctypes.c_longlong), ctypes.c_int,
             ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_float,
             ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
         ]
@@ -190,6 +200,14 @@ def fa_fwd_kv(q, k, v, o, lse, strides, workspace, workspace_bytes, num_splits, 
     """Raw call of the general forward: N query rows against Nk key rows."""
     return lib().fa_fwd_kv(q, k, v, o, lse, _strides_arg(strides, 12), workspace, workspace_bytes, num_splits,
                            B, H, N, Nk, d, scale, causal, window_left, window_right, dtype, stream)
+
+
+def fa_fwd_kv_noalloc(q, k, v, o, lse, strides, num_splits, B, H, N, Nk, d, scale, causal, window_left,
+                      window_right, dtype, stream=None) -> int:
+    """Raw call of the allocation-free general forward (split-KV partial
+    results in the library's static device array; no workspace)."""
+    return lib().fa_fwd_kv_noalloc(q, k, v, o, lse, _strides_arg(strides, 12), num_splits, B, H, N, Nk, d, scale,
+                                   causal, window_left, window_right, dtype, stream)
 
 
 def splitkv_num_splits(B, H, N, d, causal=False, window_size=(-1, -1), dtype=FA_BF16, Nk=None):

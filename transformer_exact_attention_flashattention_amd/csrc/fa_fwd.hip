@@ -7,6 +7,7 @@
 #include <climits>
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 #include "fa.h"
 #include "fa_host.h"
@@ -92,6 +93,9 @@ extern "C" const char* fa_strerror(int status) {
       return "causal must be 0 or 1, scale finite, window sides >= -1, every query row must see a key, "
              "and outputs must not overlap inputs, each other or themselves";
     case FA_ERR_LAUNCH: return "the HIP runtime rejected the kernel launch";
+    case FA_ERR_SCRATCH:
+      return "the split-KV partial results exceed the static scratch buffer of fa_fwd_kv_noalloc "
+             "(FA_NOALLOC_SCRATCH_BYTES)";
   }
   return "unknown fa_status";
 }
@@ -345,6 +349,66 @@ extern "C" int fa_fwd_kv(const void* q, const void* k, const void* v, void* o, f
                          void* stream) {
   return fwd_general(q, k, v, o, lse, strides, workspace, workspace_bytes, num_splits, B, H, N, Nk, d, scale, causal,
                      window_left, window_right, dtype, stream);
+}
+
+// ---------------------------------------------------------------------------
+// Allocation-free split-KV forward (fa_fwd_kv_noalloc): the parts' partial
+// results go to a static device array instead of a caller workspace. Each
+// GPU the library runs on holds its own copy of the array, at its own
+// address, until the process ends. In host code `scratch` names a host-side
+// stand-in, never the device memory: kernels get the address that
+// hipGetSymbolAddress returns for the current device, looked up once per
+// device on the entry point's first call there.
+
+static __device__ __attribute__((aligned(256))) float scratch[FA_NOALLOC_SCRATCH_BYTES / sizeof(float)];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The device address of `scratch` on the current device.
+int scratch_address(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return FA_ERR_LAUNCH;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return FA_ERR_LAUNCH;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return FA_OK;
+}
+
+}  // namespace
+
+extern "C" int fa_fwd_kv_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                                 const long long* strides, int num_splits, int B, int H, int N, int Nk, int d,
+                                 float scale, int causal, int window_left, int window_right, int dtype,
+                                 void* stream) {
+  if (num_splits < 0 || num_splits > kMaxSplits) return FA_ERR_ARG;
+  FwdPlan plan;
+  int st =
+      plan_fwd(q, k, v, o, lse, strides, B, H, N, Nk, d, scale, causal, window_left, window_right, dtype, &plan);
+  if (st != FA_OK || plan.nblocks == 0) return st;
+  const int ns = num_splits == 0
+                     ? choose_splits(plan.nblocks, N, Nk, d, causal, window_left, window_right, dtype)
+                     : num_splits;
+  float* part = nullptr;
+  if (ns > 1) {
+    // Every element of the parts' region that the merge reads is written
+    // by the forward kernel first (a part with no visible key of a row
+    // writes O_s = 0, LSE_s = -inf), so nothing needs clearing.
+    if (workspace_bytes_for(B, H, N, d, ns) > (long long)FA_NOALLOC_SCRATCH_BYTES) return FA_ERR_SCRATCH;
+    void* p = nullptr;
+    st = scratch_address(&p);
+    if (st != FA_OK) return st;
+    part = (float*)p;
+  }
+  return launch_fwd(plan, q, k, v, o, lse, B, H, N, Nk, d, scale, causal, window_left, window_right, dtype, part,
+                    ns, (hipStream_t)stream);
 }
 
 extern "C" int fa_fwd_window(const void* q, const void* k, const void* v, void* o, float* lse, int B,
