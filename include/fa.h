@@ -331,9 +331,14 @@ const char* fa_strerror(int status);
 
 /*
  * fa_fwd_grid - host-only query of the launch shape fa_fwd would use:
- * writes the number of workgroups and the query rows per workgroup. Returns
- * the same status fa_fwd's argument checks would (pointers excepted). Used
- * to relate kernel timings to work units; makes no HIP call.
+ * writes the number of workgroups and the query rows of one query tile,
+ * the unit the work is divided into (128 rows for 16-bit inputs, 64 for
+ * fp32; split-KV partitions each tile's key range). A workgroup runs one
+ * tile, except in the balanced causal grid (16-bit, causal, d = 64, at
+ * least two tiles), where workgroup p runs tiles nqt - 1 - p and p of its
+ * head so that all workgroups do the same work. Returns the same status
+ * fa_fwd's argument checks would (pointers excepted). Used to relate
+ * kernel timings to work units; makes no HIP call.
  */
 int fa_fwd_grid(int B, int H, int N, int d, int causal, int dtype,
                 long long* workgroups, int* rows_per_workgroup);

@@ -132,6 +132,12 @@ def test_grid_query():
     assert fa.grid(2, 12, 256, 64, 0, 0) == (24 * 2, 128)
     assert fa.grid(1, 1, 1, 64, 0, 2) == (1, 64)
     assert fa.grid(4, 1, 4096, 64, 0, 2) == (4 * 64, 64)
+    # causal 16-bit d = 64: query tiles nqt - 1 - p and p share a workgroup
+    assert fa.grid(1, 64, 4096, 64, 1, 1) == (64 * 16, 128)
+    assert fa.grid(2, 3, 300, 64, 1, 0) == (6 * 2, 128)       # 3 tiles: pairs (2, 0) and (1, 1)
+    assert fa.grid(1, 2, 100, 64, 1, 0) == (2, 128)           # a single tile: the plain grid
+    assert fa.grid(1, 128, 2048, 128, 1, 1) == (128 * 16, 128)  # d = 128: the plain grid
+    assert fa.grid(1, 64, 4096, 64, 1, 2) == (64 * 64, 64)     # fp32: the plain grid
     with pytest.raises(fa.FaError):
         fa.grid(1, 1, 1, 80, 0, 2)
 

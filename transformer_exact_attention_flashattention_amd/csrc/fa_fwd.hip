@@ -26,12 +26,16 @@ typedef void (*fwd16_fn)(const uint16_t*, const uint16_t*, const uint16_t*, uint
 typedef void (*fwd32_fn)(const float*, const float*, const float*, float*, float*, fa::View, fa::View,
                          fa::View, fa::View, int, int, int, int, int, float, int, int, fa::SplitOut);
 
+// bal: the balanced causal grid (two query tiles per workgroup; d = 64).
 template <class T>
-fwd16_fn pick16(int d, bool causal) {
+fwd16_fn pick16(int d, bool causal, bool bal) {
   switch (d) {
-    case 64: return causal ? fa::fwd16_kernel<T, 64, true> : fa::fwd16_kernel<T, 64, false>;
-    case 128: return causal ? fa::fwd16_kernel<T, 128, true> : fa::fwd16_kernel<T, 128, false>;
-    case 256: return causal ? fa::fwd16_kernel<T, 256, true> : fa::fwd16_kernel<T, 256, false>;
+    case 64:
+      return bal ? fa::fwd16_kernel<T, 64, true, true>
+                 : (causal ? fa::fwd16_kernel<T, 64, true, false> : fa::fwd16_kernel<T, 64, false, false>);
+    case 128:
+      return causal ? fa::fwd16_kernel<T, 128, true, false> : fa::fwd16_kernel<T, 128, false, false>;
+    case 256: return causal ? fa::fwd16_kernel<T, 256, true, false> : fa::fwd16_kernel<T, 256, false, false>;
   }
   return nullptr;
 }
@@ -59,6 +63,18 @@ constexpr int kMaxSplits = 64;
 
 // Query rows per workgroup of the kernel that serves dtype.
 int rows_per_block(int dtype) { return dtype == FA_F32 ? fa::kBr32 : fa::kBr; }
+
+// The balanced causal grid (fwd16_kernel with BAL: query tiles nqt - 1 - p
+// and p in one workgroup, every workgroup the same work) serves 16-bit
+// causal calls with d = 64, at least two query tiles, no left window bound
+// and no split: measured 3% faster than the plain grid's longest-first
+// order on B1 H64 N4096, bitwise the same. At d = 128 the two were within
+// 1.3% either way (the plain grid faster on the GPT-3 shape), and at d = 256
+// (one workgroup per compute unit) the plain order already hides the
+// imbalance, so those keep the plain grid.
+bool balanced_grid(int d, int dtype, int causal, int nqt, int window_left, int nsplit) {
+  return dtype != FA_F32 && d == 64 && causal && nqt >= 2 && window_left < 0 && nsplit <= 1;
+}
 
 // Checks that do not involve pointers. Fills the launch shape on success.
 int check_shape(int B, int H, int N, int d, int causal, int dtype, long long* nblocks, int* nqt) {
@@ -106,7 +122,8 @@ extern "C" int fa_fwd_grid(int B, int H, int N, int d, int causal, int dtype, lo
   int nqt = 0;
   const int st = check_shape(B, H, N, d, causal, dtype, &nblocks, &nqt);
   if (st != FA_OK) return st;
-  if (workgroups) *workgroups = nblocks;
+  const bool bal = balanced_grid(d, dtype, causal, nqt, -1, 1);
+  if (workgroups) *workgroups = bal ? nblocks / nqt * ((nqt + 1) / 2) : nblocks;
   if (rows_per_workgroup) *rows_per_workgroup = rows_per_block(dtype);
   return FA_OK;
 }
@@ -211,7 +228,9 @@ int launch_fwd(const FwdPlan& plan, const void* q, const void* k, const void* v,
                float* part, int nsplit, hipStream_t stream) {
   // log2(e) is folded into the scale: exp(x * scale) == exp2(x * c).
   const float c = (float)((double)scale * 1.4426950408889634074);
-  int h_arg = H, n_arg = N, nk_arg = Nk, nqt_arg = plan.nqt, nb_arg = (int)plan.nblocks;
+  const bool bal = balanced_grid(d, dtype, causal, plan.nqt, window_left, nsplit);
+  const long long grid = bal ? plan.nblocks / plan.nqt * ((plan.nqt + 1) / 2) : plan.nblocks;
+  int h_arg = H, n_arg = N, nk_arg = Nk, nqt_arg = plan.nqt, nb_arg = (int)grid;
   float c_arg = c;
   // Visible keys of the query at position p: p - wl .. p + wr, an unbounded
   // side as 2^30 (positions are below 2^30, so no sum with a side overflows).
@@ -232,10 +251,10 @@ int launch_fwd(const FwdPlan& plan, const void* q, const void* k, const void* v,
     fn = (const void*)pick32(d, causal != 0);
     merge = pick_merge<float>(d);
   } else if (dtype == FA_BF16) {
-    fn = (const void*)pick16<fa::Bf16>(d, causal != 0);
+    fn = (const void*)pick16<fa::Bf16>(d, causal != 0, bal);
     merge = pick_merge<fa::Bf16>(d);
   } else {
-    fn = (const void*)pick16<fa::F16>(d, causal != 0);
+    fn = (const void*)pick16<fa::F16>(d, causal != 0, bal);
     merge = pick_merge<fa::F16>(d);
   }
   if (!fn || !merge) return FA_ERR_HEADDIM;
@@ -243,7 +262,7 @@ int launch_fwd(const FwdPlan& plan, const void* q, const void* k, const void* v,
   const int rpb = fa::kThreads / (d / 4);  // rows per merge workgroup
   const long long mblocks = (rows + rpb - 1) / rpb;
   if (sp.part && mblocks > INT_MAX) return FA_ERR_SHAPE;
-  if (hipLaunchKernel(fn, dim3((unsigned)plan.nblocks, (unsigned)sp.nsplit), dim3(fa::kThreads), args, 0, stream) !=
+  if (hipLaunchKernel(fn, dim3((unsigned)grid, (unsigned)sp.nsplit), dim3(fa::kThreads), args, 0, stream) !=
       hipSuccess)
     return FA_ERR_LAUNCH;
   if (sp.part) {

@@ -382,13 +382,14 @@ constexpr int kSchedMfma = 0x0008;
 constexpr int kSchedDsRead = 0x0100;
 constexpr int kSchedVmem = 0x0020;  // vector memory reads
 
+// One 128-row query tile qt of head bh: the body of fwd16_kernel, which
+// runs it once per workgroup, or twice (a long and a short causal tile) in
+// the balanced causal grid.
 template <class T, int D, bool CAUSAL>
-__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
-                          amdgpu_waves_per_eu(D >= 256 ? 1 : 2, D >= 256 ? 1 : 2)))
-void fwd16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
-                  const uint16_t* __restrict__ V, uint16_t* __restrict__ O,
-                  float* __restrict__ LSE, View vq, View vk, View vv, View vo, int H, int N, int Nk,
-                  int nqt, int nblocks, float c, int wl, int wr, SplitOut sp) {
+__device__ __forceinline__ void fwd16_tile(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+                                           const uint16_t* __restrict__ V, uint16_t* __restrict__ O,
+                                           float* __restrict__ LSE, View vq, View vk, View vv, View vo, int H,
+                                           int N, int Nk, float c, int wl, int wr, SplitOut sp, int bh, int qt) {
   using G = Geo16<D>;
   typedef short s16x4 __attribute__((ext_vector_type(4)));
   typedef __attribute__((address_space(3))) s16x4* lds_s16x4_t;
@@ -397,8 +398,6 @@ void fwd16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K
   __shared__ __attribute__((aligned(1024))) unsigned char v0s[G::kVT];
   __shared__ __attribute__((aligned(1024))) unsigned char v1s[G::kVT];
 
-  int bh, qt;
-  decode_block(nblocks, nqt, CAUSAL, bh, qt, D >= 256 ? 32 : 64);
   Q += view_base(vq, bh, H);
   O += view_base(vo, bh, H);
   LSE += (size_t)bh * N;
@@ -746,6 +745,39 @@ void fwd16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K
       }
     }
     if (hh == 0) LSE[qrow] = (m_run + __log2f(l_tot)) * kLn2;
+  }
+}
+
+// The forward kernel for 16-bit inputs. Plain grid: one workgroup per (b h,
+// 128-row query tile), mapped by decode_block. Balanced causal grid (BAL):
+// one workgroup per (b h, pair p) of query tiles nqt - 1 - p and p, run one
+// after the other, so that every workgroup sees nqt + 1 key tiles (with
+// fewer queries than keys, the same plus a constant); the middle tile of an
+// odd nqt pairs with itself and runs once. A workgroup index maps to its
+// (b h, p) with each XCD taking a contiguous run, as decode_block does for
+// equal-work grids.
+template <class T, int D, bool CAUSAL, bool BAL>
+__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
+                          amdgpu_waves_per_eu(D >= 256 ? 1 : 2, D >= 256 ? 1 : 2)))
+void fwd16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+                  const uint16_t* __restrict__ V, uint16_t* __restrict__ O,
+                  float* __restrict__ LSE, View vq, View vk, View vv, View vo, int H, int N, int Nk,
+                  int nqt, int nblocks, float c, int wl, int wr, SplitOut sp) {
+  if constexpr (BAL) {
+    const int npair = (nqt + 1) / 2;
+    int L = blockIdx.x;
+    if ((nblocks & 7) == 0) L = (L & 7) * (nblocks >> 3) + (L >> 3);
+    const int bh = L / npair;
+    const int p = L - bh * npair;
+    fwd16_tile<T, D, CAUSAL>(Q, K, V, O, LSE, vq, vk, vv, vo, H, N, Nk, c, wl, wr, sp, bh, nqt - 1 - p);
+    if (p != nqt - 1 - p) {
+      __syncthreads();  // every wave is done with the first tile's LDS stages
+      fwd16_tile<T, D, CAUSAL>(Q, K, V, O, LSE, vq, vk, vv, vo, H, N, Nk, c, wl, wr, sp, bh, p);
+    }
+  } else {
+    int bh, qt;
+    decode_block(nblocks, nqt, CAUSAL, bh, qt, D >= 256 ? 32 : 64);
+    fwd16_tile<T, D, CAUSAL>(Q, K, V, O, LSE, vq, vk, vv, vo, H, N, Nk, c, wl, wr, sp, bh, qt);
   }
 }
 
