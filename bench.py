@@ -79,6 +79,81 @@ def _load_counters():
     return t
 
 
+N_XCD = 8  # GRBM_GUI_ACTIVE comes summed over the XCDs
+
+
+def counter_rows(root):
+    """Per dispatch of every kernel in the rocprofv3 counter-collection CSVs
+    under `root`: {(file, dispatch id): {"kernel": name, "ns": duration,
+    counter: value summed over its instances}}."""
+    import csv
+    import glob
+
+    out = {}
+    for path in glob.glob(os.path.join(root, "**", "*counter_collection.csv"), recursive=True):
+        with open(path, newline="") as f:
+            for r in csv.DictReader(f):
+                key = (path, r["Dispatch_Id"])
+                d = out.setdefault(key, {"kernel": r["Kernel_Name"],
+                                         "ns": int(r["End_Timestamp"]) - int(r["Start_Timestamp"])})
+                d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    return out
+
+
+def counter_means(root, match, first=None):
+    """Mean of each counter (and of the duration, "ns") over the dispatches
+    whose kernel name contains `match`, in dispatch order, the first
+    `first` of them if given; also their count ("dispatches")."""
+    rows = [d for _, d in sorted(counter_rows(root).items(), key=lambda kv: (kv[0][0], int(kv[0][1])))
+            if match in d["kernel"]]
+    if first:
+        rows = rows[:first]
+    if not rows:
+        raise SystemExit(f"no dispatch of a kernel matching {match!r} under {root}")
+    keys = {k for d in rows for k in d if k != "kernel"}
+    means = {k: sum(d.get(k, 0.0) for d in rows) / len(rows) for k in keys}
+    means["dispatches"] = len(rows)
+    return means
+
+
+HEADLINE_KERNEL = "fwd16_kernel<fa::Bf16, 256, true"
+COPY_KERNEL = "copyBuffer"  # the runtime's device-to-device copy (bench.py --calibrate-copy: 1 GiB)
+
+
+def ingest_counters(fetch_dir, write_dir, grbm_dir):
+    """Writes TRAFFIC_FILE from three rocprofv3 runs of
+    `bench.py --steps 10 --warmup 2 --no-cpu-baseline --no-parity --no-secondary --calibrate-copy`:
+    FETCH_SIZE, WRITE_SIZE and GRBM_GUI_ACTIVE of the headline kernel. HBM
+    bytes per launch = FETCH_SIZE and WRITE_SIZE (KiB) each scaled by what
+    they read for the calibration copy of 1 GiB; clock = GRBM_GUI_ACTIVE per
+    XCD over the dispatch's traced duration."""
+    fetch = counter_means(fetch_dir, HEADLINE_KERNEL)
+    write = counter_means(write_dir, HEADLINE_KERNEL)
+    grbm = counter_means(grbm_dir, HEADLINE_KERNEL)
+    cf = counter_means(fetch_dir, COPY_KERNEL)
+    cw = counter_means(write_dir, COPY_KERNEL)
+    gib = float(1 << 30)
+    fetch_scale = gib / (cf["FETCH_SIZE"] * 1024)
+    write_scale = gib / (cw["WRITE_SIZE"] * 1024)
+    hbm = fetch["FETCH_SIZE"] * 1024 * fetch_scale + write["WRITE_SIZE"] * 1024 * write_scale
+    sclk = grbm["GRBM_GUI_ACTIVE"] / N_XCD / grbm["ns"]
+    out = {
+        "kernel": "fwd16_kernel<Bf16, 256, causal>",
+        "workload": "long-causal-d256 B=1 H=16 N=16384 d=256",
+        "kernel_sha256": kernel_source_digest(),
+        "fetch_size_kib": fetch["FETCH_SIZE"], "write_size_kib": write["WRITE_SIZE"],
+        "fetch_scale": fetch_scale, "write_scale": write_scale,
+        "hbm_bytes_per_launch": hbm,
+        "grbm_gui_active_per_dispatch": grbm["GRBM_GUI_ACTIVE"], "grbm_dispatch_ns": grbm["ns"],
+        "sclk_ghz": round(sclk, 4),
+        "dispatches": {"fetch": fetch["dispatches"], "write": write["dispatches"], "grbm": grbm["dispatches"]},
+        "source": "profiles/fwd16_bf16_causal_counters.md",
+    }
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(out, f, indent=1)
+    return out
+
+
 def load_traffic(launch_bytes_alg):
     """HBM bytes per launch from committed rocprofv3 counter runs, or None if
     they are missing or were taken on different kernel sources."""
@@ -582,7 +657,18 @@ def main():
                     help="input type of the --sweep shapes (the fp16 and bf16 matrix peaks are the same)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 1 GiB device-to-device copy 3 times, to scale HBM counters")
+    ap.add_argument("--ingest-counters", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "GRBM_DIR"),
+                    help="no GPU work: write the headline kernel's counter summary (HBM traffic, clock) from "
+                         "three rocprofv3 --pmc output directories (FETCH_SIZE, WRITE_SIZE, GRBM_GUI_ACTIVE)")
+    ap.add_argument("--counter-means", nargs=2, metavar=("DIR", "KERNEL_SUBSTRING"),
+                    help="no GPU work: print the mean of each counter per dispatch of the matching kernel")
     args = ap.parse_args()
+    if args.ingest_counters:
+        print(json.dumps(ingest_counters(*args.ingest_counters), indent=1))
+        return
+    if args.counter_means:
+        print(json.dumps(counter_means(*args.counter_means), indent=1))
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); each GPU box here has one GPU and "
               "the kernel needs no communication between GPUs", file=sys.stderr)
