@@ -83,9 +83,10 @@ N_XCD = 8  # GRBM_GUI_ACTIVE comes summed over the XCDs
 
 
 def counter_rows(root):
-    """Per dispatch of every kernel in the rocprofv3 counter-collection CSVs
-    under `root`: {(file, dispatch id): {"kernel": name, "ns": duration,
-    counter: value summed over its instances}}."""
+    """Per dispatch of every kernel in the rocprofv3 CSVs under `root`:
+    {(file, dispatch id): {"kernel": name, "ns": duration, counter: value
+    summed over its instances}} from counter-collection files, or with the
+    duration alone from kernel-trace files."""
     import csv
     import glob
 
@@ -97,15 +98,22 @@ def counter_rows(root):
                 d = out.setdefault(key, {"kernel": r["Kernel_Name"],
                                          "ns": int(r["End_Timestamp"]) - int(r["Start_Timestamp"])})
                 d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    for path in glob.glob(os.path.join(root, "**", "*kernel_trace.csv"), recursive=True):
+        with open(path, newline="") as f:
+            for r in csv.DictReader(f):
+                out[(path, r["Dispatch_Id"])] = {"kernel": r["Kernel_Name"],
+                                                 "ns": int(r["End_Timestamp"]) - int(r["Start_Timestamp"])}
     return out
 
 
-def counter_means(root, match, first=None):
+def counter_means(root, match, skip=0, first=None):
     """Mean of each counter (and of the duration, "ns") over the dispatches
-    whose kernel name contains `match`, in dispatch order, the first
-    `first` of them if given; also their count ("dispatches")."""
+    whose kernel name contains `match`, in dispatch order: `skip` of them
+    left out, then the next `first` if given; also their count
+    ("dispatches")."""
     rows = [d for _, d in sorted(counter_rows(root).items(), key=lambda kv: (kv[0][0], int(kv[0][1])))
             if match in d["kernel"]]
+    rows = rows[skip:]
     if first:
         rows = rows[:first]
     if not rows:
@@ -136,7 +144,7 @@ def ingest_counters(fetch_dir, write_dir, grbm_dir):
     fetch_scale = gib / (cf["FETCH_SIZE"] * 1024)
     write_scale = gib / (cw["WRITE_SIZE"] * 1024)
     hbm = fetch["FETCH_SIZE"] * 1024 * fetch_scale + write["WRITE_SIZE"] * 1024 * write_scale
-    sclk = grbm["GRBM_GUI_ACTIVE"] / N_XCD / grbm["ns"]
+    sclk = grbm["GRBM_GUI_ACTIVE"] / N_XCD / grbm["ns"]  # under counter collection: below the live clock
     out = {
         "kernel": "fwd16_kernel<Bf16, 256, causal>",
         "workload": "long-causal-d256 B=1 H=16 N=16384 d=256",
@@ -145,7 +153,7 @@ def ingest_counters(fetch_dir, write_dir, grbm_dir):
         "fetch_scale": fetch_scale, "write_scale": write_scale,
         "hbm_bytes_per_launch": hbm,
         "grbm_gui_active_per_dispatch": grbm["GRBM_GUI_ACTIVE"], "grbm_dispatch_ns": grbm["ns"],
-        "sclk_ghz": round(sclk, 4),
+        "sclk_ghz_profiled": round(sclk, 4),
         "dispatches": {"fetch": fetch["dispatches"], "write": write["dispatches"], "grbm": grbm["dispatches"]},
         "source": "profiles/fwd16_bf16_causal_counters.md",
     }
@@ -161,12 +169,16 @@ def load_traffic(launch_bytes_alg):
     return None if t is None else t.get("hbm_bytes_per_launch")
 
 
-def load_clock():
-    """Shader clock (GHz) the headline kernel ran at in the committed counter
-    run: GRBM_GUI_ACTIVE cycles per dispatch over the dispatch's traced
-    duration. None if missing or taken on other kernel sources."""
+def load_cycles():
+    """GPU-busy cycles per XCD of one headline launch (GRBM_GUI_ACTIVE, summed
+    over the XCDs, / 8) from the committed counter run, or None if missing
+    or taken on other kernel sources. The count is stable from run to run;
+    over the live launch time it gives the shader clock of the run at hand
+    (under counter collection the dispatch itself runs longer)."""
     t = _load_counters()
-    return None if t is None else t.get("sclk_ghz")
+    if t is None or "grbm_gui_active_per_dispatch" not in t:
+        return None
+    return t["grbm_gui_active_per_dispatch"] / N_XCD
 
 
 _SETTLE = []
@@ -660,14 +672,17 @@ def main():
     ap.add_argument("--ingest-counters", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "GRBM_DIR"),
                     help="no GPU work: write the headline kernel's counter summary (HBM traffic, clock) from "
                          "three rocprofv3 --pmc output directories (FETCH_SIZE, WRITE_SIZE, GRBM_GUI_ACTIVE)")
-    ap.add_argument("--counter-means", nargs=2, metavar=("DIR", "KERNEL_SUBSTRING"),
-                    help="no GPU work: print the mean of each counter per dispatch of the matching kernel")
+    ap.add_argument("--counter-means", nargs="+", metavar="ARG",
+                    help="no GPU work: DIR KERNEL_SUBSTRING [SKIP [COUNT]]: the mean of each counter (and of "
+                         "the duration) per dispatch of the matching kernel, from rocprofv3 CSVs under DIR")
     args = ap.parse_args()
     if args.ingest_counters:
         print(json.dumps(ingest_counters(*args.ingest_counters), indent=1))
         return
     if args.counter_means:
-        print(json.dumps(counter_means(*args.counter_means), indent=1))
+        a = args.counter_means
+        print(json.dumps(counter_means(a[0], a[1], int(a[2]) if len(a) > 2 else 0,
+                                       int(a[3]) if len(a) > 3 else None), indent=1))
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); each GPU box here has one GPU and "
@@ -737,7 +752,8 @@ def main():
     elem = 2
     alg_bytes = c["B"] * c["H"] * c["N"] * (4 * c["D"] * elem + 4)
     traffic = load_traffic(alg_bytes)
-    sclk = load_clock()
+    cycles = load_cycles()
+    sclk = None if cycles is None else round(cycles / (kern_ms * 1e-3) / 1e9, 3)
     out = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -759,7 +775,8 @@ def main():
         "at_measured_clock": None if sclk is None else {
             "sclk_ghz": sclk, "peak": round(N_CU * sclk * 1e9 * MFMA_FLOP_PER_CLK_CU / 1e12, 1),
             "frac": round(achieved / (N_CU * sclk * 1e9 * MFMA_FLOP_PER_CLK_CU / 1e12), 4),
-            "source": "GRBM_GUI_ACTIVE per dispatch / traced duration, " + os.path.relpath(TRAFFIC_FILE, ROOT)},
+            "source": "GRBM_GUI_ACTIVE per XCD and launch (" + os.path.relpath(TRAFFIC_FILE, ROOT)
+                      + ") over this run's mean launch time"},
         "kernel_ms": {"mean": round(kern_ms, 4), "min": round(per[0], 4),
                       "median": round(per[len(per) // 2], 4), "p90": round(per[int(0.9 * (len(per) - 1))], 4)},
         "parity": par,
