@@ -637,7 +637,7 @@ def bench_sweep(fa, inputs, dev, stream, no_parity, dtype="bf16"):
                     rows = np.array([0, 1, N // 2, N - 1])
                     err_o, err_l = check_parity(o[:, :1].cpu(), lse[:, :1].cpu(), q[:, :1], k[:, :1], v[:, :1], scale,
                                                 causal, rows)
-                    ok = err_o <= (1e-2 if dtype == "bf16" else 2e-3) and err_l <= 1e-3
+                    ok = err_o <= TOL_O[dtype] and err_l <= TOL_LSE
                 _, per = time_launches(step, stream, 10, 5, settle_ms=600.0)
                 ms = float(np.mean(per))
                 fl = 4.0 * H * N * N * D / (2 if causal else 1)
