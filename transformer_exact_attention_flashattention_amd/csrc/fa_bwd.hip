@@ -19,12 +19,15 @@
 //    owns one query), then dQ^T += K^T dS^T with K^T read transposed from
 //    LDS and dS^T as the B operand; it first computes its rows'
 //    D = rowsum(dO * O) and writes them to the caller's delta buffer;
-//  * dkdv_kernel: one workgroup per (batch*head, 128-key block), each wave
-//    owning 32 keys with K^T and V^T held as B operands (at d = 256 V^T is
-//    read from an LDS copy of the block's V rows instead); per 32-query
-//    step, S = Q K^T and dP = dO V^T with Q and dO from LDS, P and dS per
-//    lane (each lane owns one key), then dV^T += dO^T P and dK^T += Q^T dS
-//    with dO^T and Q^T read transposed from LDS.
+//  * dkdv8_kernel (d <= 128) and dkdv_kernel (d = 256): one workgroup per
+//    (batch*head, 128-key block); a wave owns 32 keys and takes K^T and V^T
+//    as B operands; per 32 queries, S = Q K^T and dP = dO V^T with Q and dO
+//    from LDS, P and dS per lane (each lane owns one key), then
+//    dV^T += dO^T P and dK^T += Q^T dS with dO^T and Q^T read transposed
+//    from LDS. At d <= 128 eight waves, two per SIMD, split each 64-query
+//    step by halves and add their sums at the end, with K^T and V^T read
+//    from LDS copies of the block's rows; at d = 256 four waves hold K^T in
+//    registers and read V^T from an LDS copy.
 // The index tricks are the forward's: rows of an A operand are read through
 // the permutation sigma, which makes the accumulator of one product the B
 // operand layout of the next.
@@ -131,23 +134,25 @@ struct Operands {
 // lane order; lane l of copy block b writes row (1024 / kRS) b + l / L at
 // physical chunk l % L (L = kRS / 16 lanes per row) and so fetches the
 // logical chunk (l % L) ^ swz(row) of that row (for d = 64 the second half
-// of each 256-byte row is padding, filled with a duplicate chunk). Wave w
-// issues blocks w, w + 4, ...: 16 rows apart for 256-byte rows, which all
-// share the lane's row modulo 16 and so one source offset plus 16 rows per
-// block; 8 rows apart for 512-byte rows (d = 256), whose blocks alternate
-// between two swizzles and so two source offsets.
+// of each 256-byte row is padding, filled with a duplicate chunk). With NW
+// waves, wave w issues blocks w, w + NW, ...: for 4 waves 16 rows apart
+// with 256-byte rows, which all share the lane's row modulo 16 and so one
+// source offset plus 16 rows per block, and 8 rows apart with 512-byte rows
+// (d = 256), whose blocks alternate between two swizzles and so two source
+// offsets; for 8 waves and 256-byte rows, 32 rows apart (one offset).
 // Global rows are rs >= 2D bytes apart (the row stride of the operand's
 // view); rows past the end of the sequence are outside the buffer's range.
-template <int D, int R>
+template <int D, int R, int NW = 4>
 struct TileDma {
   static constexpr int kRS = Tile<D>::kRS;
   static constexpr int kLPR = kRS / 16;    // lanes per LDS row
   static constexpr int kRPB = 1024 / kRS;  // LDS rows per copy block
-  static constexpr int kStep = 4 * kRPB;   // rows between a wave's consecutive blocks
-  static constexpr int kNOff = 16 / kStep;  // distinct swizzles among them
+  static constexpr int kStep = NW * kRPB;  // rows between a wave's consecutive blocks
+  static constexpr int kNOff = kStep >= 16 ? 1 : 16 / kStep;  // distinct swizzles among them
+  static constexpr int kPeriod = kStep * kNOff;  // rows after which a wave's offsets repeat
   static constexpr int kBlocks = R * kRS / 1024;
-  static constexpr int kPW = kBlocks / 4;  // copy instructions per wave
-  static_assert(kBlocks % 4 == 0 && kPW % kNOff == 0, "blocks per wave");
+  static constexpr int kPW = kBlocks / NW;  // copy instructions per wave
+  static_assert(kBlocks % NW == 0 && kPW % kNOff == 0 && kPeriod % 16 == 0, "blocks per wave");
 
   struct Off {
     uint32_t v[kNOff];
@@ -173,8 +178,8 @@ struct TileDma {
     const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)src, (short)0, range, kBufWord3);
 #pragma unroll
     for (int i = 0; i < kPW; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, as_lds(lds + 1024 * (wave + 4 * i)), 16,
-                                               off.v[i % kNOff] + (uint32_t)((i / kNOff) * 16) * (uint32_t)rs,
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, as_lds(lds + 1024 * (wave + NW * i)), 16,
+                                               off.v[i % kNOff] + (uint32_t)((i / kNOff) * kPeriod) * (uint32_t)rs,
                                                0, 0, 0);
 #endif
   }
@@ -386,46 +391,35 @@ void dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   }
 }
 
-// Query rows per step of the dK/dV kernel: 64, or 32 at d = 256 so that
-// the stages (of 512-byte rows) fit in LDS beside the copy of V.
-template <int D>
-constexpr int dkdv_step_rows() {
-  return D >= 256 ? 32 : 64;
-}
 constexpr int kStatSlots = 64;  // LDS floats reserved for LSE (and for delta) per stage
 
-// dK and dV for one 128-key block; wave w owns keys 32w .. 32w+31 of it.
-// One wave per SIMD: K^T, V^T and the dK^T, dV^T accumulators alone take
-// 192 registers per lane at d = 128. Query tiles (Q, dO, LSE, delta) stream
-// through a ring of LDS stages filled by direct copies: three stages,
-// issued two steps ahead, at d <= 128.
-// VL (d = 256): V^T is read from an LDS copy of the block's V rows instead
-// of registers. At d = 256 the two accumulators and the K^T, V^T operands
-// do not fit the registers together (held all in registers, the kernel
-// spilled); the V copy (64 KiB plus padding) leaves LDS room for a ring of
-// two stages only, refilled one step ahead.
-template <class T, int D, bool CAUSAL, bool VL>
+// dK and dV for one 128-key block at d = 256; wave w owns keys 32w .. 32w+31
+// of it. One wave per SIMD: the dK^T and dV^T accumulators alone take 256
+// registers per lane. K^T is held as B operands in registers; V^T is read
+// from an LDS copy of the block's V rows (with both in registers the kernel
+// spilled). Query tiles of 32 rows (Q, dO, LSE, delta) stream through two
+// LDS stages beside the V copy (64 KiB plus padding), filled one step ahead
+// by direct copies.
+template <class T, int D, bool CAUSAL>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(1, 1)))
 void dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                  const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
                  const float* __restrict__ LSE, const float* __restrict__ Dl, uint16_t* __restrict__ dK,
                  uint16_t* __restrict__ dV, View vq, View vk, View vv, View vdo, View vdk, View vdv, int H,
                  int N, int nkb, int nblocks, float c, float scale, int wl, int wr) {
+  static_assert(D == 256, "d <= 128 runs dkdv8_kernel");
   // One array per stage: Q tile, dO tile, LSE (natural log), delta. (Few
   // distinct arrays, so that the compiler can still tell the copies into
   // one stage from the reads of another and does not wait on them.)
-  constexpr bool kVL = VL;  // V^T operands from the LDS copy
-  constexpr int kStages = kVL ? 2 : 3;
-  constexpr int kQT = dkdv_step_rows<D>();
+  constexpr int kQT = 32;  // query rows per step: the stages of 512-byte rows fit beside the V copy
   constexpr int TB = kQT * Tile<D>::kRS;
   constexpr int SB = 2 * TB + 2 * kStatSlots * 4;
   __shared__ __attribute__((aligned(1024))) unsigned char st0[SB];
   __shared__ __attribute__((aligned(1024))) unsigned char st1[SB];
-  __shared__ __attribute__((aligned(1024))) unsigned char st2[kStages == 3 ? SB : 16];
   // The block's 128 V rows, rows 2d + 16 bytes apart (the 16 rows read by a
   // 16-lane phase then hit distinct banks).
   constexpr int kVS = 2 * D + 16;
-  __shared__ __attribute__((aligned(1024))) unsigned char vblk[kVL ? kBr * kVS : 16];
+  __shared__ __attribute__((aligned(1024))) unsigned char vblk[kBr * kVS];
 
   // With a causal mask the first key blocks have the most query tiles, so
   // they start first: decode_block's longest-first order (which counts
@@ -455,32 +449,22 @@ void dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   const typename Dma::Off qoff = Dma::lane_offset(wave, lane, qsb);
   const typename Dma::Off goff = Dma::lane_offset(wave, lane, gsb);
 
-  // K^T and V^T as B operands: lane (n, hh), k-step s holds row krow,
-  // columns 16s + 8hh .. +7.
-  u32x4 kf[D / 16], vf[kVL ? 1 : D / 16];
+  // K^T as B operands: lane (n, hh), k-step s holds row krow, columns
+  // 16s + 8hh .. +7.
+  u32x4 kf[D / 16];
 #pragma unroll
-  for (int s = 0; s < D / 16; ++s) {
+  for (int s = 0; s < D / 16; ++s)
     kf[s] = krow < N ? *(const u32x4*)(K + (long long)krow * vk.r + 16 * s + 8 * hh) : u32x4{0, 0, 0, 0};
-    if constexpr (!kVL)
-      vf[s] = krow < N ? *(const u32x4*)(V + (long long)krow * vv.r + 16 * s + 8 * hh) : u32x4{0, 0, 0, 0};
-  }
-  if constexpr (kVL) {
-    // V rows of the block into LDS (zeros past N); the first step's barrier
-    // makes them visible.
-    for (int i = tid; i < kBr * (D / 8); i += kThreads) {
-      const int r = i / (D / 8), ch = i - r * (D / 8);
-      const int key = kb * kBr + r;
-      const u32x4 x = key < N ? *(const u32x4*)(V + (long long)key * vv.r + 8 * ch) : u32x4{0, 0, 0, 0};
-      *(u32x4*)(vblk + r * kVS + 16 * ch) = x;
-    }
+  // V rows of the block into LDS (zeros past N); the first step's barrier
+  // makes them visible.
+  for (int i = tid; i < kBr * (D / 8); i += kThreads) {
+    const int r = i / (D / 8), ch = i - r * (D / 8);
+    const int key = kb * kBr + r;
+    const u32x4 x = key < N ? *(const u32x4*)(V + (long long)key * vv.r + 8 * ch) : u32x4{0, 0, 0, 0};
+    *(u32x4*)(vblk + r * kVS + 16 * ch) = x;
   }
   // V^T B operand of k-step s (row krow, columns 16s + 8hh .. +7).
-  auto vop = [&](int s) {
-    if constexpr (kVL)
-      return *(const u32x4*)(vblk + (32 * wave + n) * kVS + 32 * s + 16 * hh);
-    else
-      return vf[s];
-  };
+  auto vop = [&](int s) { return *(const u32x4*)(vblk + (32 * wave + n) * kVS + 32 * s + 16 * hh); };
 
   // Queries that see a key of the block: i - wl <= j <= i + wr.
   const int k_lo = kb * kBr;
@@ -494,7 +478,6 @@ void dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     for (int i = tid; i < SB / 16; i += kThreads) {
       ((u32x4*)st0)[i] = u32x4{0, 0, 0, 0};
       ((u32x4*)st1)[i] = u32x4{0, 0, 0, 0};
-      if constexpr (kStages == 3) ((u32x4*)st2)[i] = u32x4{0, 0, 0, 0};
     }
     __syncthreads();
   }
@@ -503,7 +486,6 @@ void dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
 #pragma unroll
   for (int t = 0; t < D / 32; ++t) dk[t] = dv[t] = f32x16{};
 
-  constexpr int kCopies = 2 * Dma::kPW + 2;  // per wave per step
   auto issue = [&](int qt, unsigned char* st) {
     const int qbase = qt * kQT;
     Dma::issue(Q + (long long)qbase * vq.r, N - qbase, qsb, st, qoff, wave);
@@ -517,25 +499,12 @@ void dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const unsigned char* const gs = st + TB;
     const float* const ls = (const float*)(st + 2 * TB);
     const float* const dls = ls + kStatSlots;
-    if constexpr (kStages == 3) {
-      // This step's copies landed (those issued one step later may still
-      // fly), then every wave's copies are visible.
-      wait_vmcnt<kCopies>();
-      tile_barrier();
-      // The stage of step qt - 1 is free now: refill it with step qt + 2.
-      // Past the last step the copy repeats the last step's tile, so every
-      // step issues the same copies and waits for the same count. (With a
-      // conditional copy the compiler cannot tell, at the third stage's
-      // reads, whether that stage's copies are the newest in flight, and
-      // drains every copy there.)
-      issue(min(qt + 2, qt_hi), st_next);
-    } else {
-      // Two stages: this step's copies are the only ones in flight; after
-      // the barrier the other stage (step qt - 1) takes step qt + 1.
-      wait_vmcnt<0>();
-      tile_barrier();
-      issue(min(qt + 1, qt_hi), st_next);
-    }
+    // This step's copies are the only ones in flight; after the barrier
+    // the other stage (step qt - 1) takes step qt + 1 (past the last step
+    // the copy repeats the last tile, so every step issues the same copies).
+    wait_vmcnt<0>();
+    tile_barrier();
+    issue(min(qt + 1, qt_hi), st_next);
     const int qbase = qt * kQT;
     // Skip the step if no query of it sees a key of the wave; take the
     // unmasked path if every query of it sees every key of the wave.
@@ -635,28 +604,14 @@ void dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     }
   };
 
-  // Prologue: the first two steps in flight; then three steps per turn of
-  // the ring (stage of step qt: (qt - qt_lo) % 3). With two stages: the
-  // first step in flight, then two steps per turn.
+  // The first step in flight, then two steps per turn of the ring.
   int qt = qt_lo;
-  if constexpr (kStages == 3) {
-    issue(qt_lo, st0);
-    issue(min(qt_lo + 1, qt_hi), st1);
-    for (; qt + 2 <= qt_hi; qt += 3) {
-      step(qt, st0, st2);
-      step(qt + 1, st1, st0);
-      step(qt + 2, st2, st1);
-    }
-    if (qt <= qt_hi) step(qt, st0, st2);
-    if (qt + 1 <= qt_hi) step(qt + 1, st1, st0);
-  } else {
-    issue(qt_lo, st0);
-    for (; qt + 1 <= qt_hi; qt += 2) {
-      step(qt, st0, st1);
-      step(qt + 1, st1, st0);
-    }
-    if (qt <= qt_hi) step(qt, st0, st1);
+  issue(qt_lo, st0);
+  for (; qt + 1 <= qt_hi; qt += 2) {
+    step(qt, st0, st1);
+    step(qt + 1, st1, st0);
   }
+  if (qt <= qt_hi) step(qt, st0, st1);
   // The repeated copies of the last steps land before the wave ends.
   wait_vmcnt<0>();
 
@@ -680,6 +635,307 @@ void dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   }
 }
 
+
+// dK and dV for one 128-key block with eight waves, two per SIMD (d <= 128).
+// Wave w owns keys 32 (w & 3) .. +31 of the block and the 32-query half
+// w >> 2 of every 64-query step, so the two waves of a key range (w and
+// w + 4) sum different queries into their dK^T, dV^T accumulators, and add
+// them through LDS at the end. With one wave per SIMD (dkdv_kernel) a wave
+// issues its LDS reads, exponentials, copies and products in order and
+// they add up; a second wave per SIMD fills those gaps. To fit two waves
+// (256 registers each) the K^T and V^T operands are read from LDS copies
+// of the block's K and V rows instead of registers, and the query tiles
+// stream through a ring of stages beside them: three at d = 64, two at
+// d = 128 (refilled one step ahead), for which there is room.
+constexpr int kThreads8 = 512;  // 8 waves of 64
+
+template <class T, int D, bool CAUSAL>
+__global__ __attribute__((amdgpu_flat_work_group_size(kThreads8, kThreads8), amdgpu_waves_per_eu(2, 2)))
+void dkdv8_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+                  const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
+                  const float* __restrict__ LSE, const float* __restrict__ Dl, uint16_t* __restrict__ dK,
+                  uint16_t* __restrict__ dV, View vq, View vk, View vv, View vdo, View vdk, View vdv, int H,
+                  int N, int nkb, int nblocks, float c, float scale, int wl, int wr) {
+  static_assert(D <= 128, "two waves per SIMD hold the accumulators of d <= 128 only");
+  constexpr int kStages = D <= 64 ? 3 : 2;
+  constexpr int kQT = 64;  // query rows per step
+  constexpr int TB = kQT * Tile<D>::kRS;
+  constexpr int SB = 2 * TB + 2 * kStatSlots * 4;
+  __shared__ __attribute__((aligned(1024))) unsigned char st0[SB];
+  __shared__ __attribute__((aligned(1024))) unsigned char st1[SB];
+  __shared__ __attribute__((aligned(1024))) unsigned char st2[kStages == 3 ? SB : 16];
+  // The block's 128 K and V rows, rows 2d + 16 bytes apart (the 16 rows
+  // read by a 16-lane phase then hit distinct banks).
+  constexpr int kVS = 2 * D + 16;
+  __shared__ __attribute__((aligned(1024))) unsigned char kblk[kBr * kVS];
+  __shared__ __attribute__((aligned(1024))) unsigned char vblk[kBr * kVS];
+
+  int bh, kb;
+  decode_block(nblocks, nkb, CAUSAL, bh, kb);
+  if (CAUSAL) kb = nkb - 1 - kb;
+  Q += view_base(vq, bh, H);
+  K += view_base(vk, bh, H);
+  V += view_base(vv, bh, H);
+  dO += view_base(vdo, bh, H);
+  dK += view_base(vdk, bh, H);
+  dV += view_base(vdv, bh, H);
+  LSE += (size_t)bh * N;
+  Dl += (size_t)bh * N;
+  const int qsb = 2 * vq.r, gsb = 2 * vdo.r;  // Q and dO row strides, bytes
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int kw = wave & 3;   // key range of the wave
+  const int qh = wave >> 2;  // query half of every step
+  const int n = lane & 31;
+  const int hh = lane >> 5;
+  const int key0 = kb * kBr + 32 * kw;
+  const int krow = key0 + n;
+  const Operands<D> op(lane);
+  using Dma = TileDma<D, kQT, 8>;
+  const typename Dma::Off qoff = Dma::lane_offset(wave, lane, qsb);
+  const typename Dma::Off goff = Dma::lane_offset(wave, lane, gsb);
+
+  // K and V rows of the block into LDS (zeros past N); the first step's
+  // barrier makes them visible.
+  for (int i = tid; i < kBr * (D / 8); i += kThreads8) {
+    const int r = i / (D / 8), ch = i - r * (D / 8);
+    const int key = kb * kBr + r;
+    const u32x4 kx = key < N ? *(const u32x4*)(K + (long long)key * vk.r + 8 * ch) : u32x4{0, 0, 0, 0};
+    const u32x4 vx = key < N ? *(const u32x4*)(V + (long long)key * vv.r + 8 * ch) : u32x4{0, 0, 0, 0};
+    *(u32x4*)(kblk + r * kVS + 16 * ch) = kx;
+    *(u32x4*)(vblk + r * kVS + 16 * ch) = vx;
+  }
+  // K^T and V^T B operands of k-step s: row krow, columns 16s + 8hh .. +7.
+  const int kvo = (32 * kw + n) * kVS + 16 * hh;
+  auto kop = [&](int s) { return *(const u32x4*)(kblk + kvo + 32 * s); };
+  auto vop = [&](int s) { return *(const u32x4*)(vblk + kvo + 32 * s); };
+
+  // Queries that see a key of the block: i - wl <= j <= i + wr.
+  const int k_lo = kb * kBr;
+  const int q_first = max(k_lo - wr, 0);
+  const int q_last = min(min(k_lo + kBr - 1, N - 1) + wl, N - 1);
+  const int qt_lo = q_first / kQT, qt_hi = q_last / kQT;
+
+  // Rows past N of a ragged last tile keep whatever the stage held; they
+  // are masked, and starting from zeros keeps them finite.
+  if (N % kQT != 0) {
+    for (int i = tid; i < SB / 16; i += kThreads8) {
+      ((u32x4*)st0)[i] = u32x4{0, 0, 0, 0};
+      ((u32x4*)st1)[i] = u32x4{0, 0, 0, 0};
+      if constexpr (kStages == 3) ((u32x4*)st2)[i] = u32x4{0, 0, 0, 0};
+    }
+    __syncthreads();
+  }
+
+  f32x16 dk[D / 32], dv[D / 32];
+#pragma unroll
+  for (int t = 0; t < D / 32; ++t) dk[t] = dv[t] = f32x16{};
+
+  constexpr int kCopies = 2 * Dma::kPW + 2;  // per wave per step
+  auto issue = [&](int qt, unsigned char* st) {
+    const int qbase = qt * kQT;
+    Dma::issue(Q + (long long)qbase * vq.r, N - qbase, qsb, st, qoff, wave);
+    Dma::issue(dO + (long long)qbase * vdo.r, N - qbase, gsb, st + TB, goff, wave);
+    dma_row_stat(LSE + qbase, N - qbase, (float*)(st + 2 * TB), lane);
+    dma_row_stat(Dl + qbase, N - qbase, (float*)(st + 2 * TB) + kStatSlots, lane);
+  };
+
+  auto step = [&](int qt, const unsigned char* st, unsigned char* st_next) {
+    const unsigned char* const qs = st;
+    const unsigned char* const gs = st + TB;
+    const float* const ls = (const float*)(st + 2 * TB);
+    const float* const dls = ls + kStatSlots;
+    if constexpr (kStages == 3) {
+      // This step's copies landed (those issued one step later may still
+      // fly), then every wave's copies are visible; the stage of step
+      // qt - 1 is free and takes step qt + 2 (past the last step the copy
+      // repeats the last tile, so every step waits for the same count).
+      wait_vmcnt<kCopies>();
+      tile_barrier();
+      issue(min(qt + 2, qt_hi), st_next);
+    } else {
+      // Two stages: this step's copies are the only ones in flight; after
+      // the barrier the other stage (step qt - 1) takes step qt + 1.
+      wait_vmcnt<0>();
+      tile_barrier();
+      issue(min(qt + 1, qt_hi), st_next);
+    }
+    const int qb = qt * kQT + 32 * qh;
+    // Skip the half if none of its queries sees a key of the wave; take the
+    // unmasked path if every one of them sees every key of the wave.
+    if (key0 > qb + 31 + wr || key0 + 31 < qb - wl) return;
+    const bool full = key0 + 31 < N && qb + 32 <= N && key0 + 31 <= qb + wr && key0 >= qb + 31 - wl;
+    // S = Q K^T and dP = dO V^T (queries x keys): lane (n, hh), register r
+    // holds query qb + perm_row(r, hh) and key krow.
+    f32x16 sa = {}, ga = {};
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) {
+      sa = T::mfma(op.row(qs, 32 * qh, s), kop(s), sa);
+      ga = T::mfma(op.row(gs, 32 * qh, s), vop(s), ga);
+    }
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 8, 0);
+#pragma unroll
+    for (int i = 0; i < D / 8; ++i) {
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // P = exp2(S c - lse2) on visible pairs, dS = P (dP - D); both packed
+    // as B operands: chunk cc holds queries qb + 16cc + 8hh .. +7, whose
+    // row statistics are two runs of 4 consecutive queries. An invisible
+    // pair (or a query past N) gets lse2 = +inf, hence P = 0.
+    u32x4 pp[2], dsp[2];
+    auto make_chunk = [&](int cc) {
+      float l2[8], dl[8];
+#pragma unroll
+      for (int g = 0; g < 2; ++g) {
+        const int o = 32 * qh + perm_row(8 * cc + 4 * g, hh);
+        const f32x4 a = *(const f32x4*)(ls + o);
+        const f32x4 b = *(const f32x4*)(dls + o);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          l2[4 * g + i] = a[i] * kLog2e;
+          dl[4 * g + i] = b[i];
+        }
+      }
+      if (!full) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int q = qb + perm_row(8 * cc + i, hh);
+          const bool vis = krow < N && q < N && krow <= q + wr && krow >= q - wl;
+          l2[i] = vis ? l2[i] : INFINITY;
+        }
+      }
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        float pv[2], dsv[2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const int r = 8 * cc + 2 * w + e;
+          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sa[r], c, -l2[2 * w + e]));
+          pv[e] = p;
+          dsv[e] = p * (ga[r] - dl[2 * w + e]);
+        }
+        pp[cc][w] = T::pack(pv[0], pv[1]);
+        dsp[cc][w] = T::pack(dsv[0], dsv[1]);
+      }
+    };
+    __builtin_amdgcn_s_setprio(1);
+    make_chunk(0);
+    __builtin_amdgcn_sched_barrier(0);
+    // dV^T += dO^T P and dK^T += Q^T dS over the half's two 16-query
+    // k-steps; the second chunk's exponentials run beside the first
+    // k-step's MFMAs.
+#pragma unroll
+    for (int tb = 0; tb < D / 32; ++tb) {
+      dv[tb] = T::mfma(op.tr(gs, 2 * qh, tb), pp[0], dv[tb]);
+      dk[tb] = T::mfma(op.tr(qs, 2 * qh, tb), dsp[0], dk[tb]);
+    }
+    make_chunk(1);
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 8, 0);
+#pragma unroll
+    for (int i = 0; i < D / 16; ++i) {
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedValu, 6, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_setprio(0);
+#pragma unroll
+    for (int tb = 0; tb < D / 32; ++tb) {
+      dv[tb] = T::mfma(op.tr(gs, 2 * qh + 1, tb), pp[1], dv[tb]);
+      dk[tb] = T::mfma(op.tr(qs, 2 * qh + 1, tb), dsp[1], dk[tb]);
+    }
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 8, 0);
+#pragma unroll
+    for (int i = 0; i < D / 16; ++i) {
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  int qt = qt_lo;
+  if constexpr (kStages == 3) {
+    issue(qt_lo, st0);
+    issue(min(qt_lo + 1, qt_hi), st1);
+    for (; qt + 2 <= qt_hi; qt += 3) {
+      step(qt, st0, st2);
+      step(qt + 1, st1, st0);
+      step(qt + 2, st2, st1);
+    }
+    if (qt <= qt_hi) step(qt, st0, st2);
+    if (qt + 1 <= qt_hi) step(qt + 1, st1, st0);
+  } else {
+    issue(qt_lo, st0);
+    for (; qt + 1 <= qt_hi; qt += 2) {
+      step(qt, st0, st1);
+      step(qt + 1, st1, st0);
+    }
+    if (qt <= qt_hi) step(qt, st0, st1);
+  }
+  // The repeated copies of the last steps land, and every wave is done
+  // reading the stages and the K and V copies, before they take the
+  // partial sums.
+  wait_vmcnt<0>();
+  __syncthreads();
+
+  // Wave w + 4 hands its dK^T partial to wave w, which hands back its dV^T
+  // partial: PB bytes each, 16 bytes per lane per 4 accumulator registers.
+  constexpr int PB = (D / 32) * 4 * 64 * 16;
+  static_assert(2 * PB <= SB && 2 * PB <= kBr * kVS, "partial sums fit the stage and block arrays");
+  // The upper wave's partial goes to the K or V copy, the lower wave's to a
+  // stage; each reads its partner's.
+  const bool upper = qh != 0;
+  unsigned char* const part_up = (kw < 2 ? kblk : vblk) + (kw & 1) * PB;
+  unsigned char* const part_lo = (kw < 2 ? st0 : st1) + (kw & 1) * PB;
+  auto put = [&](const f32x16(&a)[D / 32], unsigned char* dst) {
+#pragma unroll
+    for (int t = 0; t < D / 32; ++t)
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        *(f32x4*)(dst + ((4 * t + g) * 64 + lane) * 16) =
+            f32x4{a[t][4 * g], a[t][4 * g + 1], a[t][4 * g + 2], a[t][4 * g + 3]};
+  };
+  auto add = [&](f32x16(&a)[D / 32], const unsigned char* src) {
+#pragma unroll
+    for (int t = 0; t < D / 32; ++t)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const f32x4 x = *(const f32x4*)(src + ((4 * t + g) * 64 + lane) * 16);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) a[t][4 * g + i] += x[i];
+      }
+  };
+  // Rows krow of dK (lower wave, times scale) or dV (upper wave).
+  auto store = [&](const f32x16(&a)[D / 32], uint16_t* row, float f) {
+#pragma unroll
+    for (int tb = 0; tb < D / 32; ++tb) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        u32x2 o2;
+        o2.x = T::pack(a[tb][4 * g] * f, a[tb][4 * g + 1] * f);
+        o2.y = T::pack(a[tb][4 * g + 2] * f, a[tb][4 * g + 3] * f);
+        *(u32x2*)(row + 32 * tb + 8 * g + 4 * hh) = o2;
+      }
+    }
+  };
+  if (upper)
+    put(dk, part_up);
+  else
+    put(dv, part_lo);
+  __syncthreads();
+  if (upper) {
+    add(dv, part_lo);
+    if (krow < N) store(dv, dV + (long long)krow * vdv.r, 1.f);
+  } else {
+    add(dk, part_up);
+    if (krow < N) store(dk, dK + (long long)krow * vdk.r, scale);
+  }
+}
+
 }  // namespace bwd
 }  // namespace fa
 
@@ -689,14 +945,20 @@ template <class T>
 struct BwdKernels {
   const void* dq;
   const void* dkdv;
+  int dkdv_threads;
 };
 
 template <class T, int D>
 BwdKernels<T> pick_d(bool causal) {
-  // d = 256: V^T read from LDS; otherwise K^T and V^T both in registers.
-  constexpr bool VL = D >= 256;
-  return {causal ? (const void*)fa::bwd::dq_kernel<T, D, true> : (const void*)fa::bwd::dq_kernel<T, D, false>,
-          causal ? (const void*)fa::bwd::dkdv_kernel<T, D, true, VL> : (const void*)fa::bwd::dkdv_kernel<T, D, false, VL>};
+  const void* dq = causal ? (const void*)fa::bwd::dq_kernel<T, D, true> : (const void*)fa::bwd::dq_kernel<T, D, false>;
+  if constexpr (D >= 256) {
+    // One wave per SIMD, V^T read from LDS.
+    return {dq, causal ? (const void*)fa::bwd::dkdv_kernel<T, D, true> : (const void*)fa::bwd::dkdv_kernel<T, D, false>,
+            fa::kThreads};
+  } else {
+    return {dq, causal ? (const void*)fa::bwd::dkdv8_kernel<T, D, true> : (const void*)fa::bwd::dkdv8_kernel<T, D, false>,
+            fa::bwd::kThreads8};
+  }
 }
 
 template <class T>
@@ -783,12 +1045,13 @@ extern "C" int fa_bwd_strided(const void* q, const void* k, const void* v, const
 
   const void* kq;
   const void* kkv;
+  int kv_threads;
   if (dtype == FA_BF16) {
     const auto kk = pick<fa::Bf16>(d, causal != 0);
-    kq = kk.dq, kkv = kk.dkdv;
+    kq = kk.dq, kkv = kk.dkdv, kv_threads = kk.dkdv_threads;
   } else {
     const auto kk = pick<fa::F16>(d, causal != 0);
-    kq = kk.dq, kkv = kk.dkdv;
+    kq = kk.dq, kkv = kk.dkdv, kv_threads = kk.dkdv_threads;
   }
   hipStream_t st = (hipStream_t)stream;
   int h_arg = H, n_arg = N;
@@ -814,7 +1077,7 @@ extern "C" int fa_bwd_strided(const void* q, const void* k, const void* v, const
                    (void*)&view[2], (void*)&view[4], (void*)&view[6], (void*)&view[7], (void*)&h_arg,
                    (void*)&n_arg,   (void*)&nt,      (void*)&nb,      (void*)&c,       (void*)&sc,
                    (void*)&wl,      (void*)&wr};
-  if (hipLaunchKernel(kkv, dim3((unsigned)blocks), dim3(fa::kThreads), kargs, 0, st) != hipSuccess)
+  if (hipLaunchKernel(kkv, dim3((unsigned)blocks), dim3((unsigned)kv_threads), kargs, 0, st) != hipSuccess)
     return FA_ERR_LAUNCH;
   return FA_OK;
 }
