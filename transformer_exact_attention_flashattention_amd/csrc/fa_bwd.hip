@@ -376,19 +376,7 @@ void dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   }
   if (t < t_end) step(t, st0, st1);
 
-  if (qrow < N) {
-    uint16_t* row = dQ + (long long)qrow * vdq.r;
-#pragma unroll
-    for (int tb = 0; tb < D / 32; ++tb) {
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        u32x2 out;
-        out.x = T::pack(acc[tb][4 * g] * scale, acc[tb][4 * g + 1] * scale);
-        out.y = T::pack(acc[tb][4 * g + 2] * scale, acc[tb][4 * g + 3] * scale);
-        *(u32x2*)(row + 32 * tb + 8 * g + 4 * hh) = out;
-      }
-    }
-  }
+  store_row16<T>(dQ + (long long)qrow * vdq.r, acc, scale, hh, qrow < N);
 }
 
 constexpr int kStatSlots = 64;  // LDS floats reserved for LSE (and for delta) per stage
@@ -615,24 +603,8 @@ void dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   // The repeated copies of the last steps land before the wave ends.
   wait_vmcnt<0>();
 
-  if (krow < N) {
-    uint16_t* krow_k = dK + (long long)krow * vdk.r;
-    uint16_t* krow_v = dV + (long long)krow * vdv.r;
-#pragma unroll
-    for (int tb = 0; tb < D / 32; ++tb) {
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        u32x2 ok;
-        ok.x = T::pack(dk[tb][4 * g] * scale, dk[tb][4 * g + 1] * scale);
-        ok.y = T::pack(dk[tb][4 * g + 2] * scale, dk[tb][4 * g + 3] * scale);
-        *(u32x2*)(krow_k + 32 * tb + 8 * g + 4 * hh) = ok;
-        u32x2 ov;
-        ov.x = T::pack(dv[tb][4 * g], dv[tb][4 * g + 1]);
-        ov.y = T::pack(dv[tb][4 * g + 2], dv[tb][4 * g + 3]);
-        *(u32x2*)(krow_v + 32 * tb + 8 * g + 4 * hh) = ov;
-      }
-    }
-  }
+  store_row16<T>(dK + (long long)krow * vdk.r, dk, scale, hh, krow < N);
+  store_row16<T>(dV + (long long)krow * vdv.r, dv, 1.f, hh, krow < N);
 }
 
 
@@ -909,30 +881,18 @@ void dkdv8_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K
         for (int i = 0; i < 4; ++i) a[t][4 * g + i] += x[i];
       }
   };
-  // Rows krow of dK (lower wave, times scale) or dV (upper wave).
-  auto store = [&](const f32x16(&a)[D / 32], uint16_t* row, float f) {
-#pragma unroll
-    for (int tb = 0; tb < D / 32; ++tb) {
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        u32x2 o2;
-        o2.x = T::pack(a[tb][4 * g] * f, a[tb][4 * g + 1] * f);
-        o2.y = T::pack(a[tb][4 * g + 2] * f, a[tb][4 * g + 3] * f);
-        *(u32x2*)(row + 32 * tb + 8 * g + 4 * hh) = o2;
-      }
-    }
-  };
   if (upper)
     put(dk, part_up);
   else
     put(dv, part_lo);
   __syncthreads();
+  // Rows krow of dK (lower wave, times scale) or dV (upper wave).
   if (upper) {
     add(dv, part_lo);
-    if (krow < N) store(dv, dV + (long long)krow * vdv.r, 1.f);
+    store_row16<T>(dV + (long long)krow * vdv.r, dv, 1.f, hh, krow < N);
   } else {
     add(dk, part_up);
-    if (krow < N) store(dk, dK + (long long)krow * vdk.r, scale);
+    store_row16<T>(dK + (long long)krow * vdk.r, dk, scale, hh, krow < N);
   }
 }
 

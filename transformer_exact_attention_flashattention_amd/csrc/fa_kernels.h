@@ -308,6 +308,37 @@ __device__ __forceinline__ float pair_sum(float x) {
   return __uint_as_float(p[0]) + __uint_as_float(p[1]);
 }
 
+// Stores one row of a 16-bit output from the 32x32 accumulator tiles a[t]
+// (t < NT), each value times f: lane (n, hh) holds columns 32t + 8g + 4hh
+// .. +3 of the row in registers 4g .. 4g + 3. The lane pair (n, 0), (n, 1)
+// first swaps halves, so that each lane writes 16 contiguous bytes (columns
+// 32t + 8(2gp + hh) .. +7) rather than each writing 8: half the store
+// instructions, and each row segment one 32-byte piece (measured 1-3%
+// faster over the forward shapes, bitwise the same output). Every lane
+// takes part in the swaps; ok guards the stores (the two lanes of a pair
+// share the row, hence ok).
+template <class T, int NT>
+__device__ __forceinline__ void store_row16(uint16_t* row, const f32x16 (&a)[NT], float f, int hh, bool ok) {
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+#pragma unroll
+    for (int gp = 0; gp < 2; ++gp) {
+      uint32_t lo[2], hi[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        lo[h] = T::pack(a[t][8 * gp + 2 * h] * f, a[t][8 * gp + 2 * h + 1] * f);
+        hi[h] = T::pack(a[t][8 * gp + 4 + 2 * h] * f, a[t][8 * gp + 4 + 2 * h + 1] * f);
+      }
+      // Lanes 0-31 keep their own columns 8(2gp) + 0..3 and take their
+      // partner's 8(2gp) + 4..7; lanes 32-63 take their partner's
+      // 8(2gp + 1) + 0..3 and keep their own 8(2gp + 1) + 4..7.
+      const auto s0 = __builtin_amdgcn_permlane32_swap(lo[0], hi[0], false, false);
+      const auto s1 = __builtin_amdgcn_permlane32_swap(lo[1], hi[1], false, false);
+      if (ok) *(u32x4*)(row + 32 * t + 16 * gp + 8 * hh) = u32x4{s0[0], s1[0], s0[1], s1[1]};
+    }
+  }
+}
+
 // The exponent reference m (log2 units) need not be the exact running max:
 // the result is the same in exact arithmetic for any reference (the final
 // division by the running sum cancels it), and fp32/bf16 only need the P
@@ -732,20 +763,8 @@ __device__ __forceinline__ void fwd16_tile(const uint16_t* __restrict__ Q, const
     return;
   }
   const float inv = 1.0f / l_tot;
-  if (qrow < N) {
-    uint16_t* orow = O + (long long)qrow * vo.r;
-#pragma unroll
-    for (int t = 0; t < D / 32; ++t) {
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        u32x2 out;
-        out.x = T::pack(acc[t][4 * g] * inv, acc[t][4 * g + 1] * inv);
-        out.y = T::pack(acc[t][4 * g + 2] * inv, acc[t][4 * g + 3] * inv);
-        *(u32x2*)(orow + 32 * t + 8 * g + 4 * hh) = out;
-      }
-    }
-    if (hh == 0) LSE[qrow] = (m_run + __log2f(l_tot)) * kLn2;
-  }
+  store_row16<T>(O + (long long)qrow * vo.r, acc, inv, hh, qrow < N);
+  if (qrow < N && hh == 0) LSE[qrow] = (m_run + __log2f(l_tot)) * kLn2;
 }
 
 // The forward kernel for 16-bit inputs. Plain grid: one workgroup per (b h,
