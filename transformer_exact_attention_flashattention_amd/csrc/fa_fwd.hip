@@ -262,7 +262,8 @@ int launch_fwd(const FwdPlan& plan, const void* q, const void* k, const void* v,
   const int rpb = fa::kThreads / (d / 4);  // rows per merge workgroup
   const long long mblocks = (rows + rpb - 1) / rpb;
   if (sp.part && mblocks > INT_MAX) return FA_ERR_SHAPE;
-  if (hipLaunchKernel(fn, dim3((unsigned)grid, (unsigned)sp.nsplit), dim3(fa::kThreads), args, 0, stream) !=
+  const int threads = dtype == FA_F32 ? (d <= 128 ? fa::fwd32_threads<64>() : fa::fwd32_threads<256>()) : fa::kThreads;
+  if (hipLaunchKernel(fn, dim3((unsigned)grid, (unsigned)sp.nsplit), dim3((unsigned)threads), args, 0, stream) !=
       hipSuccess)
     return FA_ERR_LAUNCH;
   if (sp.part) {

@@ -805,33 +805,48 @@ void fwd16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K
 //
 // 64 query rows per workgroup, so that a small batch of long sequences
 // still gives every compute unit a workgroup. Wave w owns rows 32*(w & 1) ..
-// +31 and the key half h = w >> 1 of every 64-key tile (keys 32h .. 32h+31):
-// the two waves of a row block run the online softmax over disjoint key
-// sets, and at the end the h = 1 wave hands its (m, l, O) to the h = 0 wave
-// through LDS, which merges them with the same rescaling rule. The window
-// (query i sees keys i - wl .. i + wr) only narrows the tile range and the
-// masks.
-// LDS: ks = K tile [64][D] floats with the 16-byte chunk swizzle ch ^ (m & 7)
-// (no key permutation); vs = V tile [64][D + 8] floats, rows padded by 32
+// +31 and the 32-key block kq = w >> 1 of every iteration's keys: at d <= 128
+// an iteration stages two 64-key tiles (128 keys, 8 waves, two per SIMD),
+// at d = 256 one (64 keys, 4 waves). The waves of a row block run the
+// online softmax over disjoint key sets, and at the end the waves kq > 0
+// hand their (m, l, O) to wave 0 through LDS, which merges them with the
+// same rescaling rule. The window (query i sees keys i - wl .. i + wr) only
+// narrows the tile range and the masks; a split-KV part keeps whole 64-key
+// tiles (a block past the part's last tile is skipped).
+// LDS: ks = K keys [KT][D] floats with the 16-byte chunk swizzle ch ^ (m & 7)
+// (no key permutation); vs = V keys [KT][D + 8] floats, rows padded by 32
 // bytes so the two lane halves (keys 4 apart) land on different banks.
 constexpr int kBr32 = 64;  // query rows per fp32 workgroup
 
+// Threads of the fp32 workgroup: 8 waves (two per SIMD) at d <= 128, where
+// each 64-row block splits every 128 keys among four waves; 4 waves at
+// d = 256 (key halves of every 64 keys), whose tiles take all the LDS.
+template <int D>
+constexpr int fwd32_threads() {
+  return D <= 128 ? 512 : 256;
+}
+
 template <int D, bool CAUSAL>
-__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
-                          amdgpu_waves_per_eu(1, 1)))
+__global__ __attribute__((amdgpu_flat_work_group_size(fwd32_threads<D>(), fwd32_threads<D>()),
+                          amdgpu_waves_per_eu(D <= 128 ? 2 : 1, D <= 128 ? 2 : 1)))
 void fwd32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
                   const float* __restrict__ V, float* __restrict__ O,
                   float* __restrict__ LSE, View vq, View vk, View vv, View vo, int H, int N, int Nk,
                   int nqt, int nblocks, float c, int wl, int wr, SplitOut sp) {
+  constexpr int NT = fwd32_threads<D>();
+  constexpr int KQ = NT / 128;                // 32-key blocks per iteration (waves per row block)
+  constexpr int TPI = KQ / 2;                 // 64-key tiles per iteration
+  constexpr int KT = 32 * KQ;                 // keys staged per iteration
   constexpr int DCH = D / 4;                  // 16-byte chunks per row
   constexpr int VSTRIDE = D + 8;              // floats per padded V row
-  constexpr int KS_BYTES = kBc * D * 4;
-  constexpr int VS_BYTES = kBc * VSTRIDE * 4;
-  constexpr int CH = kBc * DCH / kThreads;    // chunks per thread, per tensor
-  constexpr bool PF = D <= 128;               // keep the next tile in VGPRs
-  // The merge area (after the loop): per row block, the h = 1 wave's
-  // accumulator (D/32 x 16 floats per lane) in ks, its m and l in vs.
-  static_assert(2 * D * 32 * 4 <= KS_BYTES && 2 * 2 * 64 * 4 <= VS_BYTES, "merge area");
+  constexpr int KS_BYTES = KT * D * 4;
+  constexpr int VS_BYTES = KT * VSTRIDE * 4;
+  constexpr int CH = KT * DCH / NT;           // chunks per thread, per tensor
+  constexpr bool PF = D <= 64;                // keep the next keys in VGPRs (at d = 128 they would spill)
+  // The merge area (after the loop), per row block and wave kq > 0: its
+  // accumulator (D/32 x 16 floats per lane), then all the m and l.
+  constexpr int XO = 32 * D;                  // floats per partial accumulator
+  static_assert((2 * (KQ - 1) * (XO + 128)) * 4 <= KS_BYTES + VS_BYTES, "merge area");
 
   __shared__ __attribute__((aligned(16))) unsigned char smem[KS_BYTES + VS_BYTES];
   unsigned char* const ks = smem;
@@ -849,7 +864,7 @@ void fwd32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int rb = wave & 1;   // row block
-  const int kh = wave >> 1;  // key half of each tile
+  const int kq = wave >> 1;  // 32-key block of each iteration
   const int n = lane & 31;
   const int hh = lane >> 5;
   const int q0 = qt * kBr32 + rb * 32;
@@ -880,7 +895,7 @@ void fwd32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
     const int k0 = kt * kBc;
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
-      const int g = tid + i * kThreads;
+      const int g = tid + i * NT;
       const int key = g / DCH, ch = g % DCH;
       const bool ok = k0 + key < Nk;
       kreg[i] = ok ? *(const f32x4*)(K + (long long)(k0 + key) * vk.r + ch * 4) : f32x4{0, 0, 0, 0};
@@ -890,7 +905,7 @@ void fwd32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
   auto swrite_regs = [&]() {
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
-      const int g = tid + i * kThreads;
+      const int g = tid + i * NT;
       const int key = g / DCH, ch = g % DCH;
       *(f32x4*)(ks + key * (D * 4) + ((ch ^ (key & 7)) << 4)) = kreg[i];
       *(f32x4*)(vs + key * VSTRIDE + ch * 4) = vreg[i];
@@ -900,7 +915,7 @@ void fwd32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
     const int k0 = kt * kBc;
 #pragma unroll 4
     for (int i = 0; i < CH; ++i) {
-      const int g = tid + i * kThreads;
+      const int g = tid + i * NT;
       const int key = g / DCH, ch = g % DCH;
       const bool ok = k0 + key < Nk;
       const f32x4 kx = ok ? *(const f32x4*)(K + (long long)(k0 + key) * vk.r + ch * 4) : f32x4{0, 0, 0, 0};
@@ -915,20 +930,22 @@ void fwd32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
 #pragma unroll
   for (int t = 0; t < D / 32; ++t) acc[t] = f32x16{};
 
+  // An iteration stages the keys of TPI 64-key tiles from kt on (the last
+  // iteration may hold keys past t_end: they are staged but not used).
   if constexpr (PF) gload(t_lo);
-  for (int kt = t_lo; kt < t_end; ++kt) {
+  for (int kt = t_lo; kt < t_end; kt += TPI) {
     if constexpr (PF) swrite_regs();
     else copy_direct(kt);
     __syncthreads();
     if constexpr (PF) {
-      if (kt + 1 < t_end) gload(kt + 1);
+      if (kt + TPI < t_end) gload(kt + TPI);
     }
-    // This wave's keys: kb .. kb + 31. A half tile no row of the wave can
-    // see is skipped.
-    const int kb = kt * kBc + 32 * kh;
-    if (kb < Nk && kb <= q0 + pos_off + 31 + wr && kb + 31 >= q0 + pos_off - wl) {
+    // This wave's keys: kb .. kb + 31. A block outside the part's tiles, or
+    // one no row of the wave can see, is skipped.
+    const int kb = kt * kBc + 32 * kq;
+    if (kt + kq / 2 < t_end && kb < Nk && kb <= q0 + pos_off + 31 + wr && kb + 31 >= q0 + pos_off - wl) {
       f32x16 s = {};
-      const int krow = 32 * kh + n;
+      const int krow = 32 * kq + n;
       const unsigned char* kr = ks + krow * (D * 4);
 #pragma unroll
       for (int u = 0; u < D / 8; ++u) {
@@ -941,7 +958,7 @@ void fwd32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
       for (int t = 0; t < D / 32; ++t) acc[t] *= alpha;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int key = 32 * kh + acc_row(r, hh);
+        const int key = 32 * kq + acc_row(r, hh);
 #pragma unroll
         for (int t = 0; t < D / 32; ++t)
           acc[t] = __builtin_amdgcn_mfma_f32_32x32x2f32(vs[key * VSTRIDE + 32 * t + n], s[r], acc[t], 0, 0, 0);
@@ -950,32 +967,53 @@ void fwd32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
     __syncthreads();
   }
 
-  // Merge the two key halves of each row block: lane l of the h = 1 wave
-  // holds the same rows and output columns as lane l of the h = 0 wave.
-  float* const xo = (float*)ks + rb * (D * 32);  // D/32 x 16 values x 64 lanes
-  float* const xm = vs + rb * 128;               // m, then l, per lane
-  if (kh == 1) {
+  // Merge the key blocks of each row block: lane l of every wave of a row
+  // block holds the same rows and output columns; waves kq > 0 hand their
+  // (m, l, O) to wave 0 through LDS, which rescales all to the largest m.
+  float* const xbase = (float*)smem;
+  auto xo = [&](int j) { return xbase + (rb * (KQ - 1) + j - 1) * XO; };  // D/32 x 16 values x 64 lanes
+  auto xm = [&](int j) { return xbase + 2 * (KQ - 1) * XO + (rb * (KQ - 1) + j - 1) * 128; };  // m, then l
+  if (kq != 0) {
+    float* const o = xo(kq);
 #pragma unroll
     for (int t = 0; t < D / 32; ++t)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) xo[(t * 16 + r) * 64 + lane] = acc[t][r];
-    xm[lane] = m_run;
-    xm[64 + lane] = l_run;
+      for (int r = 0; r < 16; ++r) o[(t * 16 + r) * 64 + lane] = acc[t][r];
+    xm(kq)[lane] = m_run;
+    xm(kq)[64 + lane] = l_run;
   }
   __syncthreads();
-  if (kh == 1) return;
+  if (kq != 0) return;
   {
-    // Either half may have seen no key of a row (then its m is -inf, l 0).
-    const float m1 = xm[lane], l1 = xm[64 + lane];
-    const float m = fmaxf(m_run, m1);
+    // Any block may have seen no key of a row (then its m is -inf, l 0).
+    float mj[KQ], lj[KQ];
+    mj[0] = m_run;
+    lj[0] = l_run;
+#pragma unroll
+    for (int j = 1; j < KQ; ++j) {
+      mj[j] = xm(j)[lane];
+      lj[j] = xm(j)[64 + lane];
+    }
+    float m = mj[0];
+#pragma unroll
+    for (int j = 1; j < KQ; ++j) m = fmaxf(m, mj[j]);
     const float m_use = m == -INFINITY ? 0.f : m;
-    const float a0 = __builtin_amdgcn_exp2f(m_run - m_use);
-    const float a1 = __builtin_amdgcn_exp2f(m1 - m_use);
+    float a[KQ];
+#pragma unroll
+    for (int j = 0; j < KQ; ++j) a[j] = __builtin_amdgcn_exp2f(mj[j] - m_use);
 #pragma unroll
     for (int t = 0; t < D / 32; ++t)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[t][r] = a0 * acc[t][r] + a1 * xo[(t * 16 + r) * 64 + lane];
-    l_run = a0 * l_run + a1 * l1;
+      for (int r = 0; r < 16; ++r) {
+        float x = a[0] * acc[t][r];
+#pragma unroll
+        for (int j = 1; j < KQ; ++j) x += a[j] * xo(j)[(t * 16 + r) * 64 + lane];
+        acc[t][r] = x;
+      }
+    float l = a[0] * lj[0];
+#pragma unroll
+    for (int j = 1; j < KQ; ++j) l += a[j] * lj[j];
+    l_run = l;
     m_run = m;
   }
 
