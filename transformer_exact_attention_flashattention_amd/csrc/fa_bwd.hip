@@ -739,82 +739,78 @@ void dkdv8_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K
     // unmasked path if every one of them sees every key of the wave.
     if (key0 > qb + 31 + wr || key0 + 31 < qb - wl) return;
     const bool full = key0 + 31 < N && qb + 32 <= N && key0 + 31 <= qb + wr && key0 >= qb + 31 - wl;
-    // S = Q K^T and dP = dO V^T (queries x keys): lane (n, hh), register r
-    // holds query qb + perm_row(r, hh) and key krow.
+    // S = Q K^T, then dP = dO V^T (queries x keys): lane (n, hh), register
+    // r holds query qb + perm_row(r, hh) and key krow. P = exp2(S c - lse2)
+    // only needs S, so its exponentials run beside the dP products.
     f32x16 sa = {}, ga = {};
 #pragma unroll
-    for (int s = 0; s < D / 16; ++s) {
-      sa = T::mfma(op.row(qs, 32 * qh, s), kop(s), sa);
-      ga = T::mfma(op.row(gs, 32 * qh, s), vop(s), ga);
-    }
-    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 8, 0);
-#pragma unroll
-    for (int i = 0; i < D / 8; ++i) {
-      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    // P = exp2(S c - lse2) on visible pairs, dS = P (dP - D); both packed
-    // as B operands: chunk cc holds queries qb + 16cc + 8hh .. +7, whose
-    // row statistics are two runs of 4 consecutive queries. An invisible
-    // pair (or a query past N) gets lse2 = +inf, hence P = 0.
-    u32x4 pp[2], dsp[2];
-    auto make_chunk = [&](int cc) {
-      float l2[8], dl[8];
-#pragma unroll
-      for (int g = 0; g < 2; ++g) {
-        const int o = 32 * qh + perm_row(8 * cc + 4 * g, hh);
-        const f32x4 a = *(const f32x4*)(ls + o);
-        const f32x4 b = *(const f32x4*)(dls + o);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          l2[4 * g + i] = a[i] * kLog2e;
-          dl[4 * g + i] = b[i];
-        }
-      }
-      if (!full) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const int q = qb + perm_row(8 * cc + i, hh);
-          const bool vis = krow < N && q < N && krow <= q + wr && krow >= q - wl;
-          l2[i] = vis ? l2[i] : INFINITY;
-        }
-      }
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        float pv[2], dsv[2];
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          const int r = 8 * cc + 2 * w + e;
-          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sa[r], c, -l2[2 * w + e]));
-          pv[e] = p;
-          dsv[e] = p * (ga[r] - dl[2 * w + e]);
-        }
-        pp[cc][w] = T::pack(pv[0], pv[1]);
-        dsp[cc][w] = T::pack(dsv[0], dsv[1]);
-      }
-    };
-    __builtin_amdgcn_s_setprio(1);
-    make_chunk(0);
-    __builtin_amdgcn_sched_barrier(0);
-    // dV^T += dO^T P and dK^T += Q^T dS over the half's two 16-query
-    // k-steps; the second chunk's exponentials run beside the first
-    // k-step's MFMAs.
-#pragma unroll
-    for (int tb = 0; tb < D / 32; ++tb) {
-      dv[tb] = T::mfma(op.tr(gs, 2 * qh, tb), pp[0], dv[tb]);
-      dk[tb] = T::mfma(op.tr(qs, 2 * qh, tb), dsp[0], dk[tb]);
-    }
-    make_chunk(1);
+    for (int s = 0; s < D / 16; ++s) sa = T::mfma(op.row(qs, 32 * qh, s), kop(s), sa);
     __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 8, 0);
 #pragma unroll
     for (int i = 0; i < D / 16; ++i) {
       __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
       __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
-      __builtin_amdgcn_sched_group_barrier(kSchedValu, 6, 0);
     }
     __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_setprio(0);
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) ga = T::mfma(op.row(gs, 32 * qh, s), vop(s), ga);
+    // Row statistics of the lane's 16 queries (4 runs of 4 consecutive); an
+    // invisible pair (or a query past N) gets lse2 = +inf, hence P = 0.
+    float pr[16];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const f32x4 la = *(const f32x4*)(ls + 32 * qh + perm_row(4 * g, hh));
+#pragma unroll
+      for (int i = 0; i < 4; ++i) pr[4 * g + i] = la[i] * kLog2e;
+    }
+    if (!full) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int q = qb + perm_row(r, hh);
+        const bool vis = krow < N && q < N && krow <= q + wr && krow >= q - wl;
+        pr[r] = vis ? pr[r] : INFINITY;
+      }
+    }
+    u32x4 pp[2], dsp[2];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) pr[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sa[r], c, -pr[r]));
+#pragma unroll
+    for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+      for (int w = 0; w < 4; ++w) pp[cc][w] = T::pack(pr[8 * cc + 2 * w], pr[8 * cc + 2 * w + 1]);
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 8, 0);
+#pragma unroll
+    for (int i = 0; i < D / 16; ++i) {
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedValu, 8, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // dS = P (dP - D), packed as the B operand of dK.
+#pragma unroll
+    for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+      for (int g = 0; g < 2; ++g) {
+        const f32x4 da = *(const f32x4*)(dls + 32 * qh + perm_row(8 * cc + 4 * g, hh));
+        const int r = 8 * cc + 4 * g;
+        dsp[cc][2 * g] = T::pack(pr[r] * (ga[r] - da[0]), pr[r + 1] * (ga[r + 1] - da[1]));
+        dsp[cc][2 * g + 1] = T::pack(pr[r + 2] * (ga[r + 2] - da[2]), pr[r + 3] * (ga[r + 3] - da[3]));
+      }
+    __builtin_amdgcn_sched_barrier(0);
+    // dV^T += dO^T P and dK^T += Q^T dS over the half's two 16-query
+    // k-steps.
+#pragma unroll
+    for (int tb = 0; tb < D / 32; ++tb) {
+      dv[tb] = T::mfma(op.tr(gs, 2 * qh, tb), pp[0], dv[tb]);
+      dk[tb] = T::mfma(op.tr(qs, 2 * qh, tb), dsp[0], dk[tb]);
+    }
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 8, 0);
+#pragma unroll
+    for (int i = 0; i < D / 16; ++i) {
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int tb = 0; tb < D / 32; ++tb) {
       dv[tb] = T::mfma(op.tr(gs, 2 * qh + 1, tb), pp[1], dv[tb]);
