@@ -326,6 +326,30 @@ def cpu_baseline(q, k, v, scale, causal, heads):
     return cpu_baseline_entry({"N": N, "D": D, "H": q.shape[1], "causal": causal}, heads, dt)
 
 
+def cpu_small_configs(inputs):
+    """The fp64 oracle as it stands, plain (three-step definition) and tiled
+    (the online-softmax recurrence, Br = Bc = 64), timed on the three small
+    workloads (every head, every row): seconds and TFLOP/s of metric flops."""
+    from oracle import attention_ref, attention_tiled_ref
+
+    out = {}
+    for cfg in (1, 2, 3):
+        c = inputs.CONFIGS[cfg]
+        q, k, v = (t.double().numpy() for t in inputs.make_config(cfg))
+        scale = 1.0 / math.sqrt(c["D"])
+        if cfg == 1:
+            attention_ref(q, k, v, scale, c["causal"])  # untimed: starts the BLAS threads
+        flops = metric_flops(c)
+        entry = {}
+        for kind, fn in (("plain", attention_ref), ("tiled", attention_tiled_ref)):
+            t0 = time.perf_counter()
+            fn(q, k, v, scale, c["causal"])
+            dt = time.perf_counter() - t0
+            entry[kind] = {"s": round(dt, 4), "TFLOP/s": flops / dt / 1e12}
+        out[c["name"]] = entry
+    return out
+
+
 def input_digests(q, k, v):
     from transformer_exact_attention_flashattention_amd import inputs
 
@@ -860,6 +884,8 @@ def main():
         else:
             log(f"[bench] CPU baseline: fp64 oracle on {args.cpu_heads} head(s)")
             out["cpu_baseline"] = cpu_baseline(q, k, v, scale, True, args.cpu_heads)
+        log("[bench] CPU baseline: plain and tiled fp64 oracle on the three small workloads")
+        out["cpu_baseline"]["small_workloads"] = cpu_small_configs(inputs)
     print(json.dumps(out), flush=True)
     failed = [par["ok"]] + [out[k]["parity_ok"] for k in ("secondary", "fp32", "window", "backward", "packed",
                                                           "splitkv", "decode")
