@@ -66,7 +66,8 @@ typedef enum {
  * stream   a hipStream_t, or NULL for the default stream.
  *
  * Ownership: the caller allocates and owns every buffer. The library
- * allocates nothing, keeps no state between calls and is reentrant.
+ * allocates nothing for this call, which keeps no state between calls and is
+ * reentrant.
  * o and lse must not overlap q, k or v.
  *
  * Synchronisation: asynchronous. The kernel is enqueued and the call returns;
