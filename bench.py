@@ -11,12 +11,15 @@ against the fp64 oracle, and beside it against a CPU model of the kernel's
 roundings (tests/kernel_model.py). The oracle's run on the headline workload
 is timed on the host cores and reported as the CPU baseline. The other five
 workloads' outputs are checked the same way before they are timed, and the
-SHA-256 of every input tensor is reported.
+SHA-256 of every input tensor is reported. After them, the headline and a plain bf16
+matrix product run back to back for 2 s each with the board's socket power
+read beside them (the "power" entry; --no-power skips it).
 
 Prints ONE JSON line. Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
 
 import argparse
+import glob
 import hashlib
 import json
 import math
@@ -227,6 +230,92 @@ def time_launches(fn, stream, steps, warmup, settle_ms=600.0):
     wall = time.perf_counter() - t0
     per = sorted(s.elapsed_time(e) for s, e in zip(starts, ends))
     return wall, per
+
+
+def hwmon_power_dir():
+    """The first GPU hwmon directory that reports the board's socket power
+    (power1_input, microwatts; read-only telemetry), or None."""
+    for d in sorted(glob.glob("/sys/class/drm/card*/device/hwmon/hwmon*")):
+        if os.path.exists(os.path.join(d, "power1_input")):
+            return d
+    return None
+
+
+def power_run(fn, flops, seconds, hw):
+    """Runs fn back to back for about `seconds` while a thread reads the
+    socket power every 20 ms; returns the rate and the mean power over the
+    middle half of the samples (the first and last quarter straddle the
+    ramps)."""
+    import threading
+
+    import torch
+
+    samples, stop = [], threading.Event()
+
+    def poll():
+        path = os.path.join(hw, "power1_input")
+        while not stop.is_set():
+            try:
+                with open(path) as fh:
+                    samples.append(float(fh.read()) / 1e6)
+            except (OSError, ValueError):
+                pass
+            stop.wait(0.02)
+
+    for _ in range(3):
+        fn()
+    torch.cuda.synchronize()
+    th = threading.Thread(target=poll, daemon=True)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    n = 0
+    th.start()
+    e0.record()
+    t_end = time.perf_counter() + seconds
+    while time.perf_counter() < t_end:
+        for _ in range(8):
+            fn()
+        n += 8
+        torch.cuda.synchronize()
+    e1.record()
+    torch.cuda.synchronize()
+    stop.set()
+    th.join()
+    ms = e0.elapsed_time(e1) / n
+    mid = samples[len(samples) // 4: 3 * len(samples) // 4] or samples
+    return {"calls": n, "ms_per_call": round(ms, 4), "tflops": round(flops / (ms * 1e-3) / 1e12, 1),
+            "socket_w": round(sum(mid) / len(mid), 1) if mid else None, "samples": len(mid)}
+
+
+def power_context(fa, c, q, k, v, scale, dev, seconds=2.0):
+    """The headline forward and a plain bf16 8192^3 matrix product (the
+    vendor GEMM through torch.mm), each run back to back for `seconds`, with
+    the socket power beside them: what the board's power cap lets a dense
+    bf16 workload reach on this GPU."""
+    import torch
+
+    hw = hwmon_power_dir()
+    if hw is None:
+        return None
+    cap = None
+    try:
+        with open(os.path.join(hw, "power1_cap")) as fh:
+            cap = float(fh.read()) / 1e6
+    except (OSError, ValueError):
+        pass
+    qd, kd, vd = (t.to(dev) for t in (q, k, v))
+    o = torch.empty_like(qd)
+    lse = torch.empty(qd.shape[:3], dtype=torch.float32, device=dev)
+    att = power_run(lambda: fa.fwd(qd, kd, vd, softmax_scale=scale, causal=c["causal"], out=o, lse=lse),
+                    metric_flops(c), seconds, hw)
+    a = torch.randn(8192, 8192, generator=torch.Generator().manual_seed(0)).to(dev, torch.bfloat16)
+    b = torch.empty_like(a)
+    gemm = power_run(lambda: torch.mm(a, a, out=b), 2.0 * 8192 ** 3, seconds, hw)
+    del qd, kd, vd, o, lse, a, b
+    return {"cap_w": cap, "headline": att, "gemm_bf16_8192": gemm,
+            "gemm_frac_of_peak": round(gemm["tflops"] / PEAK_BF16_TFLOPS, 4),
+            "headline_vs_gemm": round(att["tflops"] / gemm["tflops"], 4),
+            "source": "hwmon power1_input (socket power) read every 20 ms over " + f"{seconds:g}"
+                      + " s of back-to-back calls, middle half averaged"}
 
 
 def check_parity(o, lse, q, k, v, scale, causal, rows, window=(-1, -1)):
@@ -691,6 +780,9 @@ def main():
                          "N = 2k..16k, d = 64/128/256, causal or not (--sweep-dtype, bf16 by default)")
     ap.add_argument("--sweep-dtype", choices=("bf16", "f16"), default="bf16",
                     help="input type of the --sweep shapes (the fp16 and bf16 matrix peaks are the same)")
+    ap.add_argument("--no-power", action="store_true",
+                    help="skip the power entry (the headline and a bf16 GEMM run back to back for 2 s each "
+                         "with the socket power read beside them)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 1 GiB device-to-device copy 3 times, to scale HBM counters")
     ap.add_argument("--ingest-counters", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "GRBM_DIR"),
@@ -870,6 +962,9 @@ def main():
         out["graph"] = bench_graph(fa, inputs, dev, stream, args.no_parity)
         out["decode"] = bench_decode(fa, inputs, dev, stream, max(args.steps, 20), args.warmup, args.no_parity)
         out["splitkv"] = bench_splitkv(fa, inputs, dev, stream, max(args.steps, 20), args.warmup, args.no_parity)
+    if not args.no_power:
+        log("[bench] power: headline and a bf16 GEMM back to back, socket power read beside them")
+        out["power"] = power_context(fa, c, q, k, v, scale, dev)
     if args.calibrate_copy:
         log("[bench] copy calibration: 3 x 1 GiB device-to-device copy")
         src = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)

@@ -83,3 +83,15 @@ def test_committed_traffic_file_is_well_formed(bench):
         t = json.load(f)
     assert len(t["kernel_sha256"]) == 64
     assert t["hbm_bytes_per_launch"] > 0
+
+
+def test_hwmon_power_dir(bench, tmp_path, monkeypatch):
+    hw = tmp_path / "card0" / "device" / "hwmon" / "hwmon3"
+    hw.mkdir(parents=True)
+    (tmp_path / "card1" / "device" / "hwmon" / "hwmon0").mkdir(parents=True)  # no power reading
+    pattern = str(tmp_path / "card*" / "device" / "hwmon" / "hwmon*")
+    real_glob = bench.glob.glob
+    monkeypatch.setattr(bench.glob, "glob", lambda p: real_glob(pattern))
+    assert bench.hwmon_power_dir() is None
+    (hw / "power1_input").write_text("1387000000\n")
+    assert bench.hwmon_power_dir() == str(hw)

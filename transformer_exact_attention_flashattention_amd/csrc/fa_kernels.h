@@ -541,7 +541,8 @@ __device__ __forceinline__ void fwd16_tile(const uint16_t* __restrict__ Q, const
       sc0 = T::mfma(*(const u32x4*)(kp + 32 * s), qf[s], sc0);
       sc1 = T::mfma(*(const u32x4*)(kp + 32 * G::kSK + 32 * s), qf[s], sc1);
     }
-    constexpr int kEvery = NVMEM > 0 && (D / 8) / NVMEM > 0 ? (D / 8) / NVMEM : 1;
+    constexpr int kDiv = NVMEM > 0 ? NVMEM : 1;
+    constexpr int kEvery = (D / 8) / kDiv > 0 ? (D / 8) / kDiv : 1;
     __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 8, 0);
 #pragma unroll
     for (int i = 0; i < D / 8; ++i) {
