@@ -194,6 +194,27 @@ def test_reference_moves_on_growing_logits(dtype, D):
     check(o, lse, q, k, v, scale, True, window=(300, -1))
 
 
+@pytest.mark.parametrize("D", [64, 128, 256])
+def test_reference_moves_on_growing_logits_f32(D):
+    """The same growing-logit inputs in fp32. At d <= 128 the fp32 kernel keeps
+    the lazy exponent reference too (the reference moves for a row whose P
+    sum over a 32-key block exceeds 2^8), at d = 256 the exact running max.
+    The stated fp32 bound applies (measured: at most 6e-6)."""
+    N = 700
+    q, k, v = inputs.make_qkv(1, 2, N, D, "f32", seed=21)
+    ramp = torch.linspace(0.05, 4.0, N).view(1, 1, N, 1)
+    k = k * ramp
+    v = v * 0.25
+    scale = 2.0 / math.sqrt(D)
+    s2 = np64(q)[0, 0] @ np64(k)[0, 0].T * scale * math.log2(math.e)
+    assert ((s2.max(axis=1) - s2[:, :32].max(axis=1)) > 8).mean() > 0.9
+    for causal in (False, True):
+        o, lse = run(q, k, v, scale, causal)
+        check(o, lse, q, k, v, scale, causal)
+    o, lse = run(q, k, v, scale, True, window=(300, -1))
+    check(o, lse, q, k, v, scale, True, window=(300, -1))
+
+
 # ----------------------------------------------------- GPU-side invariants --
 
 @pytest.mark.parametrize("dtype", ["f16", "bf16", "f32"])
