@@ -974,14 +974,43 @@ void fwd32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
 #pragma unroll
         for (int j = 0; j < 4; ++j) s = __builtin_amdgcn_mfma_f32_32x32x2f32(a[j], qf[u][j], s, 0, 0, 0);
       }
-      // O^T += V^T P^T, the V operand one float per lane per product.
+      // O^T += V^T P^T, the V operand one float per lane per product. At
+      // d <= 128 the V floats go through a ring of registers, read RING
+      // products ahead (bitwise the same result; 1-2% faster at d = 128).
       auto pv = [&](const f32x16& p) {
+        if constexpr (D >= 256) {  // no register left for reads ahead
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
+          for (int r = 0; r < 16; ++r) {
+            const int key = 32 * kq + acc_row(r, hh);
+#pragma unroll
+            for (int t = 0; t < D / 32; ++t)
+              acc[t] = __builtin_amdgcn_mfma_f32_32x32x2f32(vs[key * VSTRIDE + 32 * t + n], p[r], acc[t], 0, 0, 0);
+          }
+          return;
+        }
+        constexpr int RING = 4;
+        float va[RING][D / 32];
+        auto vload = [&](int r) {
           const int key = 32 * kq + acc_row(r, hh);
 #pragma unroll
+          for (int t = 0; t < D / 32; ++t) va[r % RING][t] = vs[key * VSTRIDE + 32 * t + n];
+        };
+#pragma unroll
+        for (int r = 0; r < RING; ++r) vload(r);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+#pragma unroll
           for (int t = 0; t < D / 32; ++t)
-            acc[t] = __builtin_amdgcn_mfma_f32_32x32x2f32(vs[key * VSTRIDE + 32 * t + n], p[r], acc[t], 0, 0, 0);
+            acc[t] = __builtin_amdgcn_mfma_f32_32x32x2f32(va[r % RING][t], p[r], acc[t], 0, 0, 0);
+          if (r + RING < 16) vload(r + RING);
+        }
+        // Keep the reads RING steps ahead: the scheduler would otherwise put
+        // each read next to its products and wait for it there.
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, RING * (D / 64), 0);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          __builtin_amdgcn_sched_group_barrier(kSchedMfma, D / 32, 0);
+          __builtin_amdgcn_sched_group_barrier(kSchedDsRead, D / 64, 0);
         }
       };
       if constexpr (D >= 256) {
