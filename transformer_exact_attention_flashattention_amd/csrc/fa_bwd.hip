@@ -191,7 +191,9 @@ struct TileDma {
 // half is the next step's and is not read.)
 __device__ __forceinline__ void dma_row_stat(const float* src, int nvalid, float* lds, int lane) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  const int rows = nvalid < 64 ? (nvalid > 0 ? nvalid : 0) : 64;
+  // The range is the same for every lane; readfirstlane lets the compiler
+  // see that, which spares a loop over lanes around the copy.
+  const int rows = __builtin_amdgcn_readfirstlane(nvalid < 64 ? (nvalid > 0 ? nvalid : 0) : 64);
   const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)src, (short)0, rows * 4, kBufWord3);
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, as_lds(lds), 4, (uint32_t)(4 * lane), 0, 0, 0);
 #endif
@@ -538,7 +540,7 @@ void dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int q = qb + perm_row(r, hh);
-          const bool vis = krow < N && q < N && krow <= q + wr && krow >= q - wl;
+          const bool vis = (krow < N) & (q < N) & (krow <= q + wr) & (krow >= q - wl);
           l2[r] = vis ? l2[r] : INFINITY;
         }
       }
@@ -740,22 +742,20 @@ void dkdv8_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K
     if (key0 > qb + 31 + wr || key0 + 31 < qb - wl) return;
     const bool full = key0 + 31 < N && qb + 32 <= N && key0 + 31 <= qb + wr && key0 >= qb + 31 - wl;
     // S = Q K^T, then dP = dO V^T (queries x keys): lane (n, hh), register
-    // r holds query qb + perm_row(r, hh) and key krow. P = exp2(S c - lse2)
-    // only needs S, so its exponentials run beside the dP products.
+    // r holds query qb + perm_row(r, hh) and key krow. The S chain's operand
+    // reads all go out before its products: asked to interleave them one or
+    // two products ahead, the compiler kept each read next to its product
+    // and waited for it there (1-8% slower over d = 64..256). P =
+    // exp2(S c - lse2) only needs S, so its exponentials are scheduled with
+    // the dP products; pairs a row may not see are set to 0 after that
+    // block, whose mask branch would otherwise split it.
     f32x16 sa = {}, ga = {};
 #pragma unroll
     for (int s = 0; s < D / 16; ++s) sa = T::mfma(op.row(qs, 32 * qh, s), kop(s), sa);
-    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 8, 0);
-#pragma unroll
-    for (int i = 0; i < D / 16; ++i) {
-      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
-    }
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2 * (D / 16), 0);
+    __builtin_amdgcn_sched_group_barrier(kSchedMfma, D / 16, 0);
     __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int s = 0; s < D / 16; ++s) ga = T::mfma(op.row(gs, 32 * qh, s), vop(s), ga);
-    // Row statistics of the lane's 16 queries (4 runs of 4 consecutive); an
-    // invisible pair (or a query past N) gets lse2 = +inf, hence P = 0.
+    // Row statistics of the lane's 16 queries (4 runs of 4 consecutive).
     float pr[16];
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
@@ -763,29 +763,31 @@ void dkdv8_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K
 #pragma unroll
       for (int i = 0; i < 4; ++i) pr[4 * g + i] = la[i] * kLog2e;
     }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) ga = T::mfma(op.row(gs, 32 * qh, s), vop(s), ga);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) pr[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sa[r], c, -pr[r]));
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2 * (D / 16), 0);
+#pragma unroll
+    for (int i = 0; i < D / 16; ++i) {
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedValu, 4, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
     if (!full) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int q = qb + perm_row(r, hh);
-        const bool vis = krow < N && q < N && krow <= q + wr && krow >= q - wl;
-        pr[r] = vis ? pr[r] : INFINITY;
+        const bool vis = (krow < N) & (q < N) & (krow <= q + wr) & (krow >= q - wl);
+        pr[r] = vis ? pr[r] : 0.f;
       }
     }
     u32x4 pp[2], dsp[2];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) pr[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sa[r], c, -pr[r]));
-#pragma unroll
     for (int cc = 0; cc < 2; ++cc)
 #pragma unroll
       for (int w = 0; w < 4; ++w) pp[cc][w] = T::pack(pr[8 * cc + 2 * w], pr[8 * cc + 2 * w + 1]);
-    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 8, 0);
-#pragma unroll
-    for (int i = 0; i < D / 16; ++i) {
-      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
-      __builtin_amdgcn_sched_group_barrier(kSchedValu, 8, 0);
-    }
-    __builtin_amdgcn_sched_barrier(0);
     // dS = P (dP - D), packed as the B operand of dK.
 #pragma unroll
     for (int cc = 0; cc < 2; ++cc)
