@@ -1022,6 +1022,15 @@ void fwd32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
         for (int t = 0; t < D / 32; ++t) acc[t] *= alpha;
         pv(s);
       } else {
+        // A 32x32x2 fp32 product writes its result over 16 passes, and a
+        // vector instruction may read it only 18 wait states after the
+        // product issues (what the compiler leaves on straight-line code).
+        // On the taken-branch paths into the mask test and past it the
+        // compiler left only 12, and a variant with such a path gave wrong
+        // results; 22 are stated here, on every path, before S is read.
+        __builtin_amdgcn_sched_barrier(0);
+        asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 5" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
         // Keys the row may not see (outside qpos - wl .. qpos + wr, or past
         // the end) get -inf, only in blocks that hold such keys.
         const int qp = qrow + pos_off, q0p = q0 + pos_off;
