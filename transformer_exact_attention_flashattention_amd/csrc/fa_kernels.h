@@ -1027,9 +1027,10 @@ void fwd32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
         // product issues (what the compiler leaves on straight-line code).
         // On the taken-branch paths into the mask test and past it the
         // compiler left only 12, and a variant with such a path gave wrong
-        // results; 22 are stated here, on every path, before S is read.
+        // results. 14 are stated here, on every path; the mask test's own
+        // scalar instructions after them bring every path to 20 or more.
         __builtin_amdgcn_sched_barrier(0);
-        asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 5" ::: "memory");
+        asm volatile("s_nop 7\n\ts_nop 5" ::: "memory");
         __builtin_amdgcn_sched_barrier(0);
         // Keys the row may not see (outside qpos - wl .. qpos + wr, or past
         // the end) get -inf, only in blocks that hold such keys.
