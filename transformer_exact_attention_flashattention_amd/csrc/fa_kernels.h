@@ -238,45 +238,71 @@ __device__ __forceinline__ float online_softmax(f32x16& s, float c, int kb, int 
 //
 // LDS holds two stages of K and two of V (separate arrays, so the compiler
 // can tell a copy into one stage from reads of the other). Tile rows are keys
-// in order; K rows are 2D + 16 bytes apart, V rows 2D + 64 bytes apart. The
-// padding puts the 16 rows read by one 16-lane ds_read_b128 phase (K) and
-// the 4 rows x 64 bytes read by one 32-lane ds_read_b64_tr_b16 phase (V) on
-// distinct banks, and lets every LDS read use one base register plus
-// immediate offsets. Tiles are copied by buffer_load_dwordx4 ... lds: each
-// wave instruction fills 1 KiB of LDS, 16 bytes per lane in lane order, and
-// each lane fetches the global chunk that belongs at its slot (pad slots
-// fetch nothing: see tile_src). Global rows are any 16-byte multiple
-// apart (the row stride of the operand's view), so a head of a packed
-// tensor is read in place.
+// in order. The layout keeps the 16 rows read by one 16-lane ds_read_b128
+// phase (K) and the 4 rows x 64 bytes read by one 32-lane
+// ds_read_b64_tr_b16 phase (V) on distinct banks:
+// - d <= 128: rows 2d bytes apart with no padding; 16-byte chunk c of row r
+//   sits at chunk c ^ chunk_swz(r) of that row. A tile is a whole number of
+//   4 KiB, so each of the 4 waves issues d/32 copies per tile, all of them
+//   moving data.
+// - d = 256: K rows 2d + 16 bytes apart, V rows 2d + 64, in order, so that
+//   every read is one base register plus immediate offsets. (The swizzle
+//   needs 8 offsets per lane for K and 8 for V; with 128 KiB of stages,
+//   beyond the reach of the 16-bit immediate, that cost the d = 256
+//   kernel 15%.) Tiles are rounded up to whole 4 KiB; pad slots and the
+//   filler past the 64 rows fetch nothing (tile_src).
+// Tiles are copied by buffer_load_dwordx4 ... lds: each wave instruction
+// fills 1 KiB of LDS, 16 bytes per lane in lane order, and each lane fetches
+// the global chunk that belongs at its slot. Global rows are any 16-byte
+// multiple apart (the row stride of the operand's view), so a head of a
+// packed tensor is read in place.
 
 template <int D>
 struct Geo16 {
-  static constexpr int kRowB = 2 * D;         // bytes of one K/V row's values
-  static constexpr int kSK = kRowB + 16;      // LDS K row stride
-  static constexpr int kSV = kRowB + 64;      // LDS V row stride
+  static constexpr bool kSwz = D <= 128;                 // unpadded, swizzled rows
+  static constexpr int kRowB = 2 * D;                    // bytes of one K/V row's values
+  static constexpr int kSK = kSwz ? kRowB : kRowB + 16;  // LDS K row stride
+  static constexpr int kSV = kSwz ? kRowB : kRowB + 64;  // LDS V row stride
   // LDS bytes of a K (V) tile, rounded up to whole 4 KiB so that each of the
-  // 4 waves issues the same number of 1 KiB copies; slots past the 64 rows
-  // are filler nobody reads.
+  // 4 waves issues the same number of 1 KiB copies.
   static constexpr int kKT = (kBc * kSK + 4095) / 4096 * 4096;
   static constexpr int kVT = (kBc * kSV + 4095) / 4096 * 4096;
-  static constexpr int kKPW = kKT / 4096;     // 1 KiB copies per wave per K tile
+  static constexpr int kKPW = kKT / 4096;  // 1 KiB copies per wave per K tile
   static constexpr int kVPW = kVT / 4096;
 };
 
+// Chunk swizzle of LDS row r (a function of r mod 16). Rows of 256 bytes:
+// ((r & 3) << 2) | ((r >> 2) & 3), a bijection of the 16 rows onto 0..15.
+// Rows of 128 bytes (d = 64, two rows per 256-byte bank period):
+// (((r >> 1) & 1) << 2) | ((r >> 2) & 3), a bijection of the 8 even (and of
+// the 8 odd) rows onto 0..7. tests/test_lds_layout.py checks coverage and
+// bank conflicts of every copy and read pattern on the host.
+template <int D>
+__device__ __forceinline__ int chunk_swz(int r) {
+  if constexpr (D == 64)
+    return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+  else
+    return ((r & 3) << 2) | ((r >> 2) & 3);
+}
+
 // Source byte offset (relative to the tile's first row, global rows rs
-// bytes apart) of LDS slot t of a tile whose LDS rows are STRIDE bytes
-// apart. Pad slots and the filler past the 64 rows get an offset beyond any
-// tile's buffer range (at most 63 rows of 2^25 bytes plus one row), so the
-// range check makes them load zeros without touching memory; their LDS
-// bytes are never read. (Measured: bitwise the same output, 0.5% faster at
-// d = 256 than fetching a real chunk again.)
+// bytes apart) of LDS slot t (16 bytes) of a tile whose LDS rows are STRIDE
+// bytes apart. Padded layout: pad slots and the filler past the 64 rows get
+// an offset beyond any tile's buffer range (at most 63 rows of 2^25 bytes
+// plus one row), so the range check makes them load zeros without touching
+// memory; their LDS bytes are never read. (Measured: bitwise the same
+// output, 0.5% faster at d = 256 than fetching a real chunk again.)
 template <int D, int STRIDE>
 __device__ __forceinline__ uint32_t tile_src(int t, int rs) {
   constexpr int R = STRIDE / 16;  // 16-byte slots per LDS row
   const int m = t / R;
   const int q = t - m * R;
-  if (q >= D / 8 || m >= kBc) return 0x7FFFFFF0u;  // pad slot or filler
-  return (uint32_t)m * (uint32_t)rs + (uint32_t)(16 * q);
+  if constexpr (STRIDE == 2 * D) {
+    return (uint32_t)m * (uint32_t)rs + (uint32_t)(16 * (q ^ chunk_swz<D>(m)));
+  } else {
+    if (q >= D / 8 || m >= kBc) return 0x7FFFFFF0u;  // pad slot or filler
+    return (uint32_t)m * (uint32_t)rs + (uint32_t)(16 * q);
+  }
 }
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
@@ -516,12 +542,47 @@ __device__ __forceinline__ void fwd16_tile(const uint16_t* __restrict__ Q, const
     copy_tile<D, G::kVPW>(vg + (long long)(kt * kBc) * vsb, Nk - kt * kBc, vsb, dst, voff, wave);
   };
 
-  // Per-lane LDS read bases. K: MFMA row n holds key sigma(n) (second tile:
-  // +32), chunk hh. V (transposed read): 16-lane block b addresses keys
-  // 8*(b>>1) + (lane&15)/4 and columns 16*(b&1) + 4*(lane&3).
-  const int kofs = sigma(n) * G::kSK + 16 * hh;
-  const int vb = lane >> 4, vj = lane & 15;
-  const int vofs = (8 * (vb >> 1) + (vj >> 2)) * G::kSV + 32 * (vb & 1) + 8 * (vj & 3);
+  // Per-lane LDS read offsets. K: MFMA row n holds key sigma(n) (keys
+  // 32..63: 32 rows further), k-step s reads its chunk 2s + hh. V
+  // (transposed read): 16-lane block b reads keys 8*(b>>1) + (lane&15)/4
+  // (+4 for the second read) of each 16-key step and, in the 32-column
+  // group t, columns 32t + 16*(b&1) + 4*(lane&3) .. +3, i.e. chunk
+  // 4t + 2*(b&1) + (lane&3)/2. Padded layout: one base each plus
+  // immediates. Swizzled layout: one offset per k-step (K) and per column
+  // group and read (V).
+  constexpr bool kSwz = G::kSwz;
+  constexpr int kNKO = kSwz ? D / 16 : 1;
+  constexpr int kNVO = kSwz ? D / 32 : 1;
+  int kofs[kNKO], vofs[2][kNVO];
+  {
+    const int vb = lane >> 4, vj = lane & 15;
+    const int vr = 8 * (vb >> 1) + (vj >> 2);
+    if constexpr (kSwz) {
+      const int ksw = chunk_swz<D>(sigma(n));
+#pragma unroll
+      for (int s = 0; s < kNKO; ++s) kofs[s] = sigma(n) * G::kSK + 16 * ((2 * s + hh) ^ ksw);
+      const int vx = 2 * (vb & 1) + ((vj & 3) >> 1);
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int vsw = chunk_swz<D>(vr + 4 * h);
+#pragma unroll
+        for (int t = 0; t < kNVO; ++t)
+          vofs[h][t] = (vr + 4 * h) * G::kSV + 16 * ((4 * t + vx) ^ vsw) + 8 * (vj & 1);
+      }
+    } else {
+      kofs[0] = sigma(n) * G::kSK + 16 * hh;
+      vofs[0][0] = vr * G::kSV + 32 * (vb & 1) + 8 * (vj & 3);
+      vofs[1][0] = vofs[0][0] + 4 * G::kSV;
+    }
+  }
+  // LDS address of k-step s of key half kh (keys 32 kh .. 32 kh + 31) in K
+  // stage ks, and of the V operand read h of 16-key step cc, column group t.
+  auto k_addr = [&](const unsigned char* ks, int s, int kh) {
+    return kSwz ? ks + kofs[s] + 32 * kh * G::kSK : ks + kofs[0] + 32 * s + 32 * kh * G::kSK;
+  };
+  auto v_addr = [&](const unsigned char* vt, int cc, int t, int h) {
+    return kSwz ? vt + 16 * cc * G::kSV + vofs[h][t] : vt + vofs[h][0] + 16 * cc * G::kSV + 64 * t;
+  };
 
   float m_run = -INFINITY, l_run = 0.f;
   f32x16 acc[D / 32];
@@ -535,11 +596,10 @@ __device__ __forceinline__ void fwd16_tile(const uint16_t* __restrict__ Q, const
     constexpr int NVMEM = decltype(nvmem)::value;
     sc0 = f32x16{};
     sc1 = f32x16{};
-    const unsigned char* kp = ks + kofs;
 #pragma unroll
     for (int s = 0; s < D / 16; ++s) {
-      sc0 = T::mfma(*(const u32x4*)(kp + 32 * s), qf[s], sc0);
-      sc1 = T::mfma(*(const u32x4*)(kp + 32 * G::kSK + 32 * s), qf[s], sc1);
+      sc0 = T::mfma(*(const u32x4*)k_addr(ks, s, 0), qf[s], sc0);
+      sc1 = T::mfma(*(const u32x4*)k_addr(ks, s, 1), qf[s], sc1);
     }
     constexpr int kDiv = NVMEM > 0 ? NVMEM : 1;
     constexpr int kEvery = (D / 8) / kDiv > 0 ? (D / 8) / kDiv : 1;
@@ -555,17 +615,14 @@ __device__ __forceinline__ void fwd16_tile(const uint16_t* __restrict__ Q, const
   // O^T += V^T P^T for one tile; the A operand comes from two transposed
   // 8-byte reads of the V tile.
   auto pv_tile = [&](const unsigned char* vt, const u32x4 (&pf)[4]) {
-    const unsigned char* vp = vt + vofs;
     // Consecutive MFMAs go to different accumulators (t inner), so none
     // waits for the previous one's result.
 #pragma unroll
     for (int cc = 0; cc < 4; ++cc) {
 #pragma unroll
       for (int t = 0; t < D / 32; ++t) {
-        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_s16x4_t)as_lds(vp + (16 * cc) * G::kSV + 64 * t));
-        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_s16x4_t)as_lds(vp + (16 * cc + 4) * G::kSV + 64 * t));
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t)as_lds(v_addr(vt, cc, t, 0)));
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t)as_lds(v_addr(vt, cc, t, 1)));
         const u32x2 l2 = __builtin_bit_cast(u32x2, lo);
         const u32x2 h2 = __builtin_bit_cast(u32x2, hi);
         const u32x4 a = {l2.x, l2.y, h2.x, h2.y};
