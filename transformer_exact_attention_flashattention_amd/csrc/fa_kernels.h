@@ -30,7 +30,8 @@
 //    rows are stored in LDS with bits 2 and 3 of the key index swapped
 //    (sigma below), which makes each lane's eight keys contiguous in V^T;
 //  * 16-bit K/V tiles of 64 keys go global -> LDS by buffer loads that write
-//    LDS directly, two stages each, with padded rows; V is read transposed
+//    LDS directly, two stages each (unpadded rows with a chunk swizzle at
+//    d <= 128, padded rows at d = 256); V is read transposed
 //    from its natural layout by ds_read_b64_tr_b16 (fp32 tiles go through
 //    registers);
 //  * causal: key tiles past the workgroup's last row are never loaded, and
