@@ -186,9 +186,11 @@ struct TileDma {
 };
 
 // Row statistics (LSE or delta) of the 64 queries from src into LDS by a
-// 4-byte copy per lane; every wave copies the same 256 bytes, so that all
-// waves issue the same number of copies. (With 32-query steps the upper
-// half is the next step's and is not read.)
+// 4-byte copy per lane (256 bytes per wave instruction). Where a step waits
+// for every copy of a wave, one wave copies them; where the wait counts
+// leave the next step's copies in flight, every wave copies the same 256
+// bytes, so that all waves issue the same number of copies. (With 32-query
+// steps the upper half is the next step's and is not read.)
 __device__ __forceinline__ void dma_row_stat(const float* src, int nvalid, float* lds, int lane) {
 #if defined(__HIP_DEVICE_COMPILE__)
   // The range is the same for every lane; readfirstlane lets the compiler
@@ -480,8 +482,12 @@ void dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const int qbase = qt * kQT;
     Dma::issue(Q + (long long)qbase * vq.r, N - qbase, qsb, st, qoff, wave);
     Dma::issue(dO + (long long)qbase * vdo.r, N - qbase, gsb, st + TB, goff, wave);
-    dma_row_stat(LSE + qbase, N - qbase, (float*)(st + 2 * TB), lane);
-    dma_row_stat(Dl + qbase, N - qbase, (float*)(st + 2 * TB) + kStatSlots, lane);
+    // Each step waits for all of a wave's copies, so one wave copies the
+    // statistics for all.
+    if (wave == 0) {
+      dma_row_stat(LSE + qbase, N - qbase, (float*)(st + 2 * TB), lane);
+      dma_row_stat(Dl + qbase, N - qbase, (float*)(st + 2 * TB) + kStatSlots, lane);
+    }
   };
 
   auto step = [&](int qt, const unsigned char* st, unsigned char* st_next) {
@@ -707,13 +713,19 @@ void dkdv8_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K
 #pragma unroll
   for (int t = 0; t < D / 32; ++t) dk[t] = dv[t] = f32x16{};
 
-  constexpr int kCopies = 2 * Dma::kPW + 2;  // per wave per step
+  constexpr int kCopies = 2 * Dma::kPW + 2;  // per wave per step (three stages)
   auto issue = [&](int qt, unsigned char* st) {
     const int qbase = qt * kQT;
     Dma::issue(Q + (long long)qbase * vq.r, N - qbase, qsb, st, qoff, wave);
     Dma::issue(dO + (long long)qbase * vdo.r, N - qbase, gsb, st + TB, goff, wave);
-    dma_row_stat(LSE + qbase, N - qbase, (float*)(st + 2 * TB), lane);
-    dma_row_stat(Dl + qbase, N - qbase, (float*)(st + 2 * TB) + kStatSlots, lane);
+    // With three stages every wave copies the (same) statistics, so that
+    // all waves issue the same number of copies for the wait counts; with
+    // two, each step waits for all of a wave's copies, and wave 0 alone
+    // copies them.
+    if (kStages == 3 || wave == 0) {
+      dma_row_stat(LSE + qbase, N - qbase, (float*)(st + 2 * TB), lane);
+      dma_row_stat(Dl + qbase, N - qbase, (float*)(st + 2 * TB) + kStatSlots, lane);
+    }
   };
 
   auto step = [&](int qt, const unsigned char* st, unsigned char* st_next) {
