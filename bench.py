@@ -352,14 +352,46 @@ def oracle_check(o, lse, q, k, v, scale, causal, dtype, window=(-1, -1), heads=N
             "heads_checked": int(qs.shape[1]), "of_heads": int(q.shape[1]), "oracle_s": round(dt, 2)}
 
 
+def _row_pmax(q, k, scale, causal):
+    """max_j P_ij per query row (fp32 on the CPU, 1024 rows at a time): the
+    weight of the row's largest score, for the model comparison's bound."""
+    import torch
+
+    qf, kf = q.float(), k.float()
+    N, Nk = qf.shape[2], kf.shape[2]
+    out = torch.empty(qf.shape[:3])
+    for r0 in range(0, N, 1024):
+        r1 = min(r0 + 1024, N)
+        s = torch.matmul(qf[:, :, r0:r1], kf.transpose(-1, -2).contiguous()) * scale
+        if causal:  # query i sits at key position i + Nk - N
+            keys = torch.arange(Nk)[None, :]
+            rows = torch.arange(r0, r1)[:, None] + (Nk - N)
+            s = s.masked_fill(keys > rows, float("-inf"))
+        m = s.max(dim=-1, keepdim=True).values
+        out[:, :, r0:r1] = 1.0 / torch.exp(s - m).sum(dim=-1)
+    return out
+
+
+# The model comparison's limits (those of the GPU test of the rounding
+# model): per element |O - O_model| <= 2 ulp(O_model) + 2 u' max_j P_ij
+# max_j |V_jc|, with u' the spacing of [1, 2) in the input type, and at most
+# this share of elements differing at all.
+MODEL_SPACING_P = {"bf16": 2.0 ** -7, "f16": 2.0 ** -10}
+MODEL_MAX_DIFFERING = {"bf16": 0.02, "f16": 0.05}
+
+
 def model_check(o, q, k, v, scale, causal, heads=None):
     """The GPU output (CPU tensor, 16-bit) against the CPU model of the
     kernel's roundings (tests/kernel_model.py) on the first `heads` heads:
     the largest difference, in absolute terms and in units of the output
-    type's spacing at the model's value, and the share of elements that
-    differ at all. The fp64 oracle stays the parity bar; this shows kernel
-    errors far smaller than the output's own rounding."""
+    type's spacing at the model's value (large where |O| is near 0, whose
+    spacing is tiny), the share of elements that differ at all, and the
+    worst ratio to the per-element bound of the GPU test of the model
+    (`model_ok`: every ratio <= 1 and the differing share within its limit).
+    The fp64 oracle stays the parity bar; this shows kernel errors far
+    smaller than the output's own rounding."""
     import numpy as np
+    import torch
 
     sys.path.insert(0, os.path.join(ROOT, "tests"))
     from kernel_model import forward_model, output_ulp
@@ -368,9 +400,16 @@ def model_check(o, q, k, v, scale, causal, heads=None):
     om, _ = forward_model(q[:, hs], k[:, hs], v[:, hs], scale, causal)
     a, b = o[:, hs].double().numpy(), om.double().numpy()
     d = np.abs(a - b)
-    ulps = d / output_ulp(b, q.dtype)
-    return {"max_abs_dO_model": float(d.max()), "max_ulps": float(ulps.max()),
-            "frac_differing": float((d > 0).mean()), "heads": int(a.shape[1])}
+    ulp = output_ulp(b, q.dtype)
+    dt = "bf16" if q.dtype == torch.bfloat16 else "f16"
+    vmax = np.abs(v[:, hs].double().numpy()).max(axis=2, keepdims=True)
+    pmax = _row_pmax(q[:, hs], k[:, hs], scale, causal).double().numpy()[..., None]
+    bound = 2 * ulp + 2 * MODEL_SPACING_P[dt] * pmax * vmax
+    frac = float((d > 0).mean())
+    worst = float((d / bound).max())
+    return {"max_abs_dO_model": float(d.max()), "max_ulps": float((d / ulp).max()),
+            "frac_differing": frac, "worst_ratio_to_model_bound": round(worst, 4),
+            "model_ok": bool(worst <= 1.0 and frac < MODEL_MAX_DIFFERING[dt]), "heads": int(a.shape[1])}
 
 
 def blas_info():
