@@ -95,3 +95,31 @@ def test_hwmon_power_dir(bench, tmp_path, monkeypatch):
     assert bench.hwmon_power_dir() is None
     (hw / "power1_input").write_text("1387000000\n")
     assert bench.hwmon_power_dir() == str(hw)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_model_check_verdict(bench, dtype):
+    """The bench's rounding-model comparison: the model's own output passes
+    with ratio 0; one element moved by 0.25 (beyond 2 ulp + 2 u' max P max|V|
+    for any |O| < 4 and |V| < 5) fails the per-element bound; a systematic
+    one-unit shift of every element stays within the bound but fails the
+    share of differing elements."""
+    import torch
+
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    from kernel_model import forward_model, output_ulp
+    from transformer_exact_attention_flashattention_amd import inputs
+
+    q, k, v = inputs.make_qkv(1, 2, 200, 64, dtype, seed=11)
+    om, _ = forward_model(q, k, v, 0.125, True)
+    r = bench.model_check(om, q, k, v, 0.125, True)
+    assert r["model_ok"] and r["worst_ratio_to_model_bound"] == 0.0 and r["frac_differing"] == 0.0
+    bad = om.clone()
+    assert float(v.abs().max()) < 5.0 and float(om.abs().max()) < 4.0
+    bad[0, 1, 100, 7] += 0.25
+    r = bench.model_check(bad, q, k, v, 0.125, True)
+    assert not r["model_ok"] and r["worst_ratio_to_model_bound"] > 1.0
+    ulp = torch.from_numpy(output_ulp(om.double().numpy(), q.dtype))
+    shifted = (om.double() + ulp).to(q.dtype)
+    r = bench.model_check(shifted, q, k, v, 0.125, True)
+    assert r["worst_ratio_to_model_bound"] <= 1.0 and r["frac_differing"] > 0.5 and not r["model_ok"]
